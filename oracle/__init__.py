@@ -1,0 +1,13 @@
+"""fp64 CPU oracle (test infrastructure only; never imported by the product path)."""
+from .lra_oracle import (  # noqa: F401
+    adapter_term,
+    attend,
+    kv_head_of,
+    lora_attention,
+    lora_attn_decode,
+    lora_attn_prefill,
+    lr_cache_build,
+    materialise_kv,
+    rope_angles,
+    rope_rotate,
+)

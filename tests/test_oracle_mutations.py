@@ -1,0 +1,109 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check that the pins
+catch every one: a pin set that lets a dropped term, a wrong sign or index,
+or a transposed operand through is too weak."""
+import numpy as np
+import pytest
+
+from oracle import lra_oracle as O
+from tests.oracle_pins import ALL_PINS
+
+_orig_rope = O.rope_rotate
+_orig_attend = O.attend
+_orig_adapter = O.adapter_term
+_orig_mat = O.materialise_kv
+
+
+def _rope_sign(x, positions, theta):
+    return _orig_rope(x, -np.asarray(positions), theta)
+
+
+def _rope_pos_shift(x, positions, theta):
+    return _orig_rope(x, np.asarray(positions) + 1, theta)
+
+
+def _rope_adjacent_pairs(x, positions, theta):
+    x = np.asarray(x, np.float64)
+    if theta == 0:
+        return x.copy()
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    inv = np.argsort(perm)
+    return _orig_rope(x[..., perm], positions, theta)[..., inv]
+
+
+def _rope_freq(x, positions, theta):
+    x = np.asarray(x, np.float64)
+    if theta == 0:
+        return x.copy()
+    d = x.shape[-1]
+    ang = np.asarray(positions, np.float64)[:, None] * np.power(theta, -np.arange(d // 2) / d)[None, :]
+    shape = (ang.shape[0],) + (1,) * (x.ndim - 2) + (d // 2,)
+    c, s = np.cos(ang).reshape(shape), np.sin(ang).reshape(shape)
+    x1, x2 = x[..., : d // 2], x[..., d // 2 :]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def _adapter_head_major(l_rows, b, Hkv, d):
+    return (np.asarray(l_rows) @ np.asarray(b)).reshape(-1, d, Hkv).transpose(0, 2, 1)
+
+
+def _drop_v_adapter(kb, vb, lk, lv, bk, bv, theta):
+    K, _ = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+    return K, np.asarray(vb, np.float64).copy()
+
+
+def _drop_k_adapter(kb, vb, lk, lv, bk, bv, theta):
+    _, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+    return np.asarray(kb, np.float64).copy(), V
+
+
+def _rope_on_v_too(kb, vb, lk, lv, bk, bv, theta):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+    T, Hkv, d = kb.shape
+    v_ad = V - vb
+    return K, vb + O.rope_rotate(v_ad, np.arange(T), theta)
+
+
+def _gqa_modulo(j, Hq, Hkv):
+    return j % Hkv
+
+
+def _causal_exclusive(q, positions, K, V, sm_scale):
+    return _orig_attend(q, np.maximum(np.asarray(positions) - 1, 0), K, V, sm_scale)
+
+
+def _no_scale(q, positions, K, V, sm_scale):
+    return _orig_attend(q, positions, K, V, 1.0)
+
+
+def _build_transposed(X, A):
+    return (np.asarray(A, np.float64).T @ np.asarray(X, np.float64).T).T[:, ::-1]
+
+
+MUTATIONS = {
+    "rope_sign": ("rope_rotate", _rope_sign),
+    "rope_position_shift": ("rope_rotate", _rope_pos_shift),
+    "rope_adjacent_pairs": ("rope_rotate", _rope_adjacent_pairs),
+    "rope_frequency_exponent": ("rope_rotate", _rope_freq),
+    "adapter_head_major_columns": ("adapter_term", _adapter_head_major),
+    "drop_value_adapter": ("materialise_kv", _drop_v_adapter),
+    "drop_key_adapter": ("materialise_kv", _drop_k_adapter),
+    "rotate_value_adapter": ("materialise_kv", _rope_on_v_too),
+    "gqa_modulo_mapping": ("kv_head_of", _gqa_modulo),
+    "causal_off_by_one": ("attend", _causal_exclusive),
+    "missing_softmax_scale": ("attend", _no_scale),
+    "build_columns_reversed": ("lr_cache_build", _build_transposed),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    attr, fn = MUTATIONS[name]
+    monkeypatch.setattr(O, attr, fn)
+    failed = []
+    for pin in ALL_PINS:
+        try:
+            pin(O)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"no pin catches mutation {name}"
