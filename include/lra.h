@@ -1,0 +1,183 @@
+/*
+ * lra.h - attention over a shared-base + low-rank KV cache on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (LRAgent: Efficient KV Cache Sharing for Multi-LoRA LLM
+ * Agents, abstract; PReCache abstract and Figure 1 caption): every cached
+ * key and value is the sum of a base part computed with the pretrained
+ * weights, shared by all agents, and an adapter part kept in its low-rank
+ * form,
+ *
+ *     K[n] = K_base[n] + rope_n(L_k[n] . B_k)      V[n] = V_base[n] + L_v[n] . B_v
+ *
+ * with L = X . A the low-rank cache of the hidden states X and (A, B) the
+ * LoRA factors of the key/value projections. The full-dimension adapter
+ * term is never written to device memory: keys are rebuilt per tile in
+ * registers, and the value term is applied once per output row as
+ * (P . L_v) . B_v (LRAgent abstract: the kernel reorders the attention
+ * computation so the low-rank cache is not expanded to full dimension).
+ *
+ * Conventions shared by every entry point
+ * - All pointers are device pointers unless marked (host).
+ * - The caller owns every buffer. The library allocates nothing, keeps no
+ *   pointer after it returns and has no state other than a thread-local
+ *   error message. Work is enqueued on `stream` (a hipStream_t; NULL is the
+ *   default stream) and the call returns without waiting; buffers must stay
+ *   alive until that work has run.
+ * - Return value: LRA_OK (0) or a negative lra_status. Argument checks run
+ *   on the host before any HIP call; nothing throws or aborts. The message
+ *   of the last failure on the calling thread is lra_last_error().
+ * - Device-side contents (block ids, agent ids, lengths) are trusted: an
+ *   out-of-range value is undefined behaviour.
+ * - dtype applies to every floating-point tensor of a call (q, pools,
+ *   adapters, out; X, A, L for the cache build). Accumulation is fp32.
+ *
+ * Cache layout (block size 16 tokens, NB physical blocks):
+ *   k_base   [NB, Hkv, 16, d]   keys of one (block, head), token-major
+ *   v_base   [NB, Hkv, d, 16]   values of one (block, head), 16 tokens of a dim contiguous
+ *   L_k pool [NB, 16, r]        token-major low-rank key rows
+ *   L_v pool [NB, r, 16]        rank-major low-rank value rows
+ *   B_k, B_v [r, Hkv*d]         per agent; column h*d + i feeds KV head h, dim i
+ * A sequence's token n lives in physical block block_tables[s][n/16], slot
+ * n%16, in the base pools and in the low-rank pools of its agent alike.
+ * Keys in k_base are stored after the rotary embedding; the adapter key
+ * term is rotated at its absolute 0-based position n (rotate-half pairing
+ * (i, i+d/2), angle n*rope_theta^(-2i/d)); values are not rotated.
+ */
+#ifndef LRA_H
+#define LRA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LRA_VERSION 100
+
+typedef enum lra_status {
+  LRA_OK = 0,
+  LRA_ERR_INVALID_ARG = -1, /* null pointer, bad size or misaligned buffer */
+  LRA_ERR_UNSUPPORTED = -2, /* valid but not built: head dim, rank, dtype, GQA ratio */
+  LRA_ERR_WORKSPACE = -3,   /* workspace smaller than the size query returned */
+  LRA_ERR_LAUNCH = -4       /* the HIP runtime rejected a launch */
+} lra_status;
+
+typedef enum lra_dtype { LRA_F32 = 0, LRA_BF16 = 1 } lra_dtype;
+
+/* Where lr_cache_build stores rows when a slot mapping is given. */
+typedef enum lra_l_layout {
+  LRA_L_TOKEN_MAJOR = 0, /* pool [NB, 16, ldl]: row of slot s at L + s*ldl (the L_k layout) */
+  LRA_L_RANK_MAJOR = 1   /* pool [NB, n_cols, 16]: column c of slot s at L + ((s/16)*n_cols + c)*16 + s%16 (the L_v layout) */
+} lra_l_layout;
+
+/* LRA_VERSION of the built library. */
+int lra_version(void);
+
+/* Message of the last failed call on this thread ("" if none). Valid until
+ * the next lra call on the same thread. */
+const char* lra_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * Low-rank cache build: L = X . A (PReCache abstract and Figure 1 caption:
+ * an agent's compact low-rank cache is precomputed from the hidden states of
+ * a context segment; LRAgent abstract: the adapter component is stored in
+ * its low-rank form).
+ *
+ *   X [n_tokens, hidden] row stride ldx, A [hidden, n_cols] row stride lda.
+ *   Products in fp32 from bf16 inputs, one fp32 sum per output, one
+ *   round-to-nearest-even to bf16 at the store.
+ *   slot_mapping == NULL: dense store, row i at L + i*ldl (token-major only).
+ *   slot_mapping != NULL: int64 [n_tokens]; row i goes to slot
+ *   slot_mapping[i] of a paged pool laid out as `l_layout` says; a negative
+ *   slot skips the row. Columns [0, n_cols) of each row are written.
+ *   dtype: LRA_BF16. hidden % 8 == 0, 1 <= n_cols <= 256, ldx, lda >= their
+ *   widths, X and A 16-byte aligned with ldx % 8 == 0.
+ *   workspace: at least lr_cache_build_workspace_size(...) bytes of device
+ *   memory (fp32 partial sums; contents on entry do not matter).
+ * ---------------------------------------------------------------------- */
+size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_cols);
+
+int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void* L, int64_t ldl,
+                   const int64_t* slot_mapping, int32_t l_layout, int32_t n_tokens, int32_t hidden,
+                   int32_t n_cols, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode attention: one query token per sequence at position T_s - 1 over
+ * keys 0..T_s-1 (T_s = context_lens[s] includes the current token).
+ *
+ *   q, out        [S, Hq, d]; q already rotated. out[s, j] for query head j
+ *                 reads KV head j / (Hq/Hkv).
+ *   block_tables  int32 [S, max_blocks]; entries past ceil(T_s/16) are not read.
+ *   context_lens  int32 [S], 1 <= T_s <= max_blocks*16 and <= max_context_len.
+ *   group_offsets int32 [num_groups+1] or NULL (every sequence its own group).
+ *                 Sequences group_offsets[g] .. group_offsets[g+1]-1 must share
+ *                 the block-table row and context length of the first one;
+ *                 the base cache is then read once for all of them (the
+ *                 shared base component of LRAgent's abstract). At most
+ *                 16 / (Hq/Hkv) sequences of a group share one pass; larger
+ *                 groups are served in several passes.
+ *   agent_ids     int32 [S], in [0, N_agents).
+ *   l_k_pools, l_v_pools
+ *                 device arrays [N_agents] of device pointers to each agent's
+ *                 low-rank pools ([NB,16,r_a] and [NB,r_a,16]). Agents with
+ *                 shared-A adapters pass the same pointers (LRAgent abstract:
+ *                 shared-A lets the low-rank cache itself be shared).
+ *   b_k, b_v      device arrays [N_agents] of device pointers to [r_a, Hkv*d].
+ *   ranks         int32 [N_agents], each in 1..max_rank; with LRA_BF16 each
+ *                 rank must be a multiple of 8 (rows are read 16 bytes at a time).
+ *   max_rank      (host) 1..64. d: 64 or 128 (bf16: 128). block_size: 16.
+ *   sm_scale      softmax scale (usually 1/sqrt(d)).
+ *   rope_theta    rotary base for the adapter key term; 0 disables it.
+ *   dtype         LRA_BF16 (split-K kernel on bf16 MFMA, fp32 accumulate) or
+ *                 LRA_F32 (fp32 throughout).
+ *   workspace     at least lora_attn_decode_workspace_size(...) bytes. Its
+ *                 first lora_attn_decode_counter_bytes(...) bytes are arrival
+ *                 counters that must be zero before the first call; every
+ *                 call leaves them zero again, so a workspace can be reused
+ *                 by later calls on the same stream. Calls that overlap in
+ *                 time must use different workspaces.
+ * ---------------------------------------------------------------------- */
+size_t lora_attn_decode_workspace_size(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
+                                       int32_t max_rank, int32_t max_context_len, int32_t dtype);
+size_t lora_attn_decode_counter_bytes(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
+                                      int32_t max_rank, int32_t max_context_len, int32_t dtype);
+
+int lora_attn_decode(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                     int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                     const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
+                     const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                     const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
+                     int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
+                     int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Prefill attention: a chunk of q_len_s = cu_q_lens[s+1] - cu_q_lens[s]
+ * new tokens per sequence, already written to the caches, attends causally:
+ * query i of sequence s sits at position T_s - q_len_s + i and sees keys
+ * 0..that position. PReCache runs adapted prefill over each agent's new
+ * segment after a shared context (Figure 1 caption).
+ *
+ *   q, out        [cu_q_lens[S], Hq, d]; cu_q_lens int32 [S+1], q_len_s <= T_s.
+ *   max_q_len     (host) >= every q_len_s.
+ *   Everything else as for decode (no grouping). dtype: LRA_BF16, d = 128.
+ *   workspace     lora_attn_prefill_workspace_size(...) bytes (may be 0,
+ *                 then workspace may be NULL).
+ * ---------------------------------------------------------------------- */
+size_t lora_attn_prefill_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_rank,
+                                        int32_t max_q_len, int32_t max_context_len, int32_t dtype);
+
+int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                      int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                      const int32_t* cu_q_lens, int32_t max_q_len, const int32_t* agent_ids,
+                      const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                      const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
+                      int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
+                      int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LRA_H */

@@ -1,0 +1,67 @@
+// Device-side helpers for gfx950 (CDNA4): vector types of the MFMA builtins,
+// bf16 packing, raw loads and cross-lane reductions over a 64-wide wavefront.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lra {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;  // 16x16x32 operand
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short i16x4;     // 16x16x16 operand
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// MFMA wrappers. Lane layout (gfx950, 64 lanes, l = lane):
+//   A operand: row l%16, k-group l/16;  B operand: column l%16, k-group l/16;
+//   accumulator: column l%16, rows 4*(l/16) + i for i = 0..3.
+// The k slots inside a group are paired between A and B by position, so any
+// fixed assignment of logical k to (group, slot) used for both is valid.
+__device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ __forceinline__ i16x4 as_i16x4(uint2 u) { return __builtin_bit_cast(i16x4, u); }
+__device__ __forceinline__ bf16x8 cat8(uint2 lo, uint2 hi) {
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Round-to-nearest-even fp32 -> bf16, two at a time (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+  bf16x2 r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return make_uint2(pack_bf16(a, b), pack_bf16(c, d));
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
+
+// Plain global loads of raw bits (vector loads; never the scalar data cache
+// for writes anywhere in this library).
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+
+__device__ __forceinline__ float wave_max_across_groups(float v) {
+  // Reduce over the 4 lane groups (lanes l, l^16, l^32, l^48) that hold the
+  // same accumulator column.
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_across_groups(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+}  // namespace lra

@@ -1,0 +1,112 @@
+// Host/device argument blocks and launcher declarations shared by the C-ABI
+// layer (lra_api.cpp) and the kernel sources. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lra {
+
+constexpr int kBlock = 16;       // tokens per cache block
+constexpr int kNumCU = 256;      // MI355X compute units (8 XCDs x 32)
+constexpr int kNumXcd = 8;       // workgroups are dealt round-robin over XCDs
+constexpr int kDecodeWaves = 4;  // waves per decode workgroup
+constexpr int kStepTokens = 32;  // tokens per wave step (two cache blocks)
+constexpr int kMaxSplits = 64;   // split-K partitions per (group, head, row tile)
+
+// Decode launch plan: derived on the host from sizes only, so the workspace
+// query and the launch agree.
+struct DecodePlan {
+  int G;            // query heads per KV head
+  int apt;          // sequences of a group served by one row tile
+  int row_tiles;    // row tiles per group (upper bound)
+  int rp;           // rank padded to the MFMA k granule (16, 32, 64)
+  int split;        // tokens per split (multiple of kDecodeWaves * kStepTokens)
+  int nsplit;       // splits for the longest context
+  int part_stride;  // floats per partial row: 4 (m, l, pad) + d + rp
+  size_t counter_bytes;
+  size_t partial_bytes;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* kb;
+  const void* vb;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* group_offsets;
+  const int32_t* agent_ids;
+  const void* const* lk;
+  const void* const* lv;
+  const void* const* bk;
+  const void* const* bv;
+  const int32_t* ranks;
+  void* out;
+  unsigned* counters;
+  float* partials;
+  int32_t max_blocks;
+  int32_t num_groups;
+  int32_t S;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t d;
+  int32_t G;
+  int32_t apt;
+  int32_t row_tiles;
+  int32_t split;
+  int32_t nsplit;
+  int32_t part_stride;
+  int32_t n_work;  // num_groups * row_tiles * nsplit * Hkv
+  float sm_scale;
+  float sm_scale_log2;  // sm_scale * log2(e)
+  int32_t rope;             // 1: rotate the adapter key term
+  double rope_log2_theta;   // log2 of the rotary base
+};
+
+struct BuildArgs {
+  const uint16_t* X;
+  const uint16_t* A;
+  void* L;
+  const int64_t* slot_mapping;
+  float* partials;
+  int64_t ldx, lda, ldl;
+  int32_t n_tokens, hidden, n_cols, layout;
+  int32_t ksplit, kchunk, row_tiles, col_tiles;
+};
+
+struct PrefillArgs {
+  const void* q;
+  const void* kb;
+  const void* vb;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* cu_q_lens;
+  const int32_t* agent_ids;
+  const void* const* lk;
+  const void* const* lv;
+  const void* const* bk;
+  const void* const* bv;
+  const int32_t* ranks;
+  void* out;
+  int32_t max_blocks;
+  int32_t S;
+  int32_t Hq;
+  int32_t Hkv;
+  int32_t d;
+  int32_t G;
+  int32_t max_q_len;
+  int32_t q_tiles;  // query tiles per sequence
+  int32_t rp;
+  float sm_scale;
+  float sm_scale_log2;
+  int32_t rope;
+  double rope_log2_theta;
+};
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, hipStream_t stream);
+hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_lr_build_bf16(const BuildArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace lra

@@ -1,0 +1,304 @@
+// C-ABI layer: host-side argument checks, launch plans and error reporting.
+// Every check here runs before the first HIP call of an entry point, so the
+// error paths can be exercised on a machine without a GPU.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/lra.h"
+#include "internal.h"
+
+namespace lra {
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return LRA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
+
+int pad_rank(int max_rank) { return max_rank <= 16 ? 16 : (max_rank <= 32 ? 32 : 64); }
+
+// Launch plan of the decode kernels; depends on host sizes only.
+DecodePlan decode_plan(int S, int num_groups, int Hq, int Hkv, int d, int max_rank, int max_ctx, int dtype) {
+  DecodePlan p{};
+  p.G = Hq / Hkv;
+  p.rp = pad_rank(max_rank);
+  if (dtype == LRA_F32) {
+    // fp32 kernel: one workgroup per (sequence, KV head), no split
+    p.apt = 1;
+    p.row_tiles = 1;
+    p.split = max_ctx;
+    p.nsplit = 1;
+    p.part_stride = 0;
+    p.counter_bytes = 0;
+    p.partial_bytes = 0;
+    return p;
+  }
+  p.apt = 16 / p.G;
+  if (p.apt > 256 / p.rp) p.apt = 256 / p.rp;  // staged B_k^T of a tile fits 64 KB of LDS
+  const int max_group = S - num_groups + 1;
+  p.row_tiles = ceil_div(max_group, p.apt);
+  const long long items = (long long)num_groups * p.row_tiles * Hkv;
+  const int granule = kDecodeWaves * kStepTokens;
+  long long split = ((long long)max_ctx * items + kNumCU - 1) / kNumCU;
+  split = (long long)round_up((size_t)split, granule);
+  if (split < granule) split = granule;
+  if (split > 4096) split = 4096;
+  if (ceil_div(max_ctx, split) > kMaxSplits) split = (long long)round_up((size_t)ceil_div(max_ctx, kMaxSplits), granule);
+  p.split = (int)split;
+  p.nsplit = ceil_div(max_ctx, split);
+  p.part_stride = 4 + d + p.rp;
+  const size_t tiles = (size_t)num_groups * p.row_tiles * Hkv;
+  p.counter_bytes = round_up(tiles * sizeof(unsigned), 256);
+  p.partial_bytes = p.nsplit > 1 ? tiles * p.nsplit * 16 * (size_t)p.part_stride * sizeof(float) : 0;
+  return p;
+}
+
+int check_decode_sizes(int S, int num_groups, int Hq, int Hkv, int d, int max_rank, int max_ctx, int dtype) {
+  if (S < 0) return fail(LRA_ERR_INVALID_ARG, "S must be >= 0 (got %d)", S);
+  if (Hq < 1 || Hkv < 1) return fail(LRA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1 (got %d, %d)", Hq, Hkv);
+  if (Hq % Hkv) return fail(LRA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (Hq / Hkv > 16) return fail(LRA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  if (dtype != LRA_F32 && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "dtype %d is not LRA_F32 or LRA_BF16", dtype);
+  if (dtype == LRA_BF16 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "bf16 kernels are built for d = 128 (got %d)", d);
+  if (dtype == LRA_F32 && d != 64 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "fp32 kernel supports d = 64 or 128 (got %d)", d);
+  if (max_rank < 1 || max_rank > 64) return fail(LRA_ERR_UNSUPPORTED, "max_rank must be in 1..64 (got %d)", max_rank);
+  if (max_ctx < 1) return fail(LRA_ERR_INVALID_ARG, "max_context_len must be >= 1 (got %d)", max_ctx);
+  if (S > 0 && (num_groups < 1 || num_groups > S))
+    return fail(LRA_ERR_INVALID_ARG, "num_groups must be in 1..S (got %d, S=%d)", num_groups, S);
+  return LRA_OK;
+}
+
+double log2_theta(float theta) { return theta > 0.f ? log2((double)theta) : 0.0; }
+
+}  // namespace
+}  // namespace lra
+
+using namespace lra;
+
+extern "C" {
+
+int lra_version(void) { return LRA_VERSION; }
+
+const char* lra_last_error(void) { return g_err; }
+
+// --------------------------------------------------------------------------
+size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_cols) {
+  if (n_tokens <= 0 || hidden <= 0 || n_cols <= 0) return 0;
+  const int row_tiles = ceil_div(n_tokens, 16);
+  int ksplit = ceil_div(kNumCU, row_tiles);
+  const int kmax = ceil_div(hidden, 256);
+  if (ksplit > kmax) ksplit = kmax;
+  if (ksplit < ceil_div(hidden, 1024)) ksplit = ceil_div(hidden, 1024);
+  if (ksplit < 1) ksplit = 1;
+  const int kchunk = (int)round_up((size_t)ceil_div(hidden, ksplit), 32);
+  ksplit = ceil_div(hidden, kchunk);
+  return (size_t)ksplit * n_tokens * n_cols * sizeof(float);
+}
+
+int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void* L, int64_t ldl,
+                   const int64_t* slot_mapping, int32_t l_layout, int32_t n_tokens, int32_t hidden,
+                   int32_t n_cols, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "lr_cache_build supports LRA_BF16 only (got %d)", dtype);
+  if (n_tokens < 0 || hidden < 1 || n_cols < 1)
+    return fail(LRA_ERR_INVALID_ARG, "bad sizes n_tokens=%d hidden=%d n_cols=%d", n_tokens, hidden, n_cols);
+  if (n_cols > 256) return fail(LRA_ERR_UNSUPPORTED, "n_cols must be <= 256 (got %d)", n_cols);
+  if (hidden % 8) return fail(LRA_ERR_UNSUPPORTED, "hidden must be a multiple of 8 (got %d)", hidden);
+  if (n_tokens == 0) return ok();
+  if (!X || !A || !L) return fail(LRA_ERR_INVALID_ARG, "X, A and L must be non-null");
+  if (!aligned16(X) || ldx % 8) return fail(LRA_ERR_INVALID_ARG, "X must be 16-byte aligned with ldx %% 8 == 0");
+  if (ldx < hidden || lda < n_cols) return fail(LRA_ERR_INVALID_ARG, "ldx (%lld) < hidden or lda (%lld) < n_cols", (long long)ldx, (long long)lda);
+  if (l_layout != LRA_L_TOKEN_MAJOR && l_layout != LRA_L_RANK_MAJOR)
+    return fail(LRA_ERR_INVALID_ARG, "unknown l_layout %d", l_layout);
+  if (!slot_mapping && l_layout != LRA_L_TOKEN_MAJOR)
+    return fail(LRA_ERR_INVALID_ARG, "a dense store (no slot mapping) is token-major only");
+  if (l_layout == LRA_L_TOKEN_MAJOR && ldl < n_cols)
+    return fail(LRA_ERR_INVALID_ARG, "ldl (%lld) < n_cols (%d)", (long long)ldl, n_cols);
+  const size_t need = lr_cache_build_workspace_size(n_tokens, hidden, n_cols);
+  if (!workspace || workspace_bytes < need)
+    return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
+  BuildArgs a{};
+  a.X = (const uint16_t*)X;
+  a.A = (const uint16_t*)A;
+  a.L = L;
+  a.slot_mapping = slot_mapping;
+  a.partials = (float*)workspace;
+  a.ldx = ldx;
+  a.lda = lda;
+  a.ldl = ldl;
+  a.n_tokens = n_tokens;
+  a.hidden = hidden;
+  a.n_cols = n_cols;
+  a.layout = l_layout;
+  a.row_tiles = ceil_div(n_tokens, 16);
+  a.col_tiles = ceil_div(n_cols, 16);
+  a.ksplit = (int)(need / ((size_t)n_tokens * n_cols * sizeof(float)));
+  a.kchunk = (int)round_up((size_t)ceil_div(hidden, a.ksplit), 32);
+  if (a.kchunk > 1024) return fail(LRA_ERR_UNSUPPORTED, "internal: hidden chunk %d too large", a.kchunk);
+  const hipError_t e = launch_lr_build_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lr_cache_build launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// --------------------------------------------------------------------------
+size_t lora_attn_decode_workspace_size(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
+                                       int32_t max_rank, int32_t max_context_len, int32_t dtype) {
+  if (S <= 0 || check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) != LRA_OK) return 0;
+  const DecodePlan p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  return p.counter_bytes + p.partial_bytes;
+}
+
+size_t lora_attn_decode_counter_bytes(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
+                                      int32_t max_rank, int32_t max_context_len, int32_t dtype) {
+  if (S <= 0 || check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) != LRA_OK) return 0;
+  return decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype).counter_bytes;
+}
+
+int lora_attn_decode(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                     int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                     const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
+                     const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                     const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
+                     int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
+                     int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!group_offsets) num_groups = S;
+  int rc = check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  if (rc != LRA_OK) return rc;
+  if (S == 0) return ok();
+  if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (N_agents < 1) return fail(LRA_ERR_INVALID_ARG, "N_agents must be >= 1 (got %d)", N_agents);
+  if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
+    return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
+  if (!q || !k_base || !v_base || !block_tables || !context_lens || !agent_ids || !l_k_pools || !l_v_pools || !b_k ||
+      !b_v || !ranks || !out)
+    return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+  if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
+    return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
+  if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
+    return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
+  const DecodePlan p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  const size_t need = p.counter_bytes + p.partial_bytes;
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed (got %zu)", need, workspace_bytes);
+
+  DecodeArgs a{};
+  a.q = q;
+  a.kb = k_base;
+  a.vb = v_base;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.group_offsets = group_offsets;
+  a.agent_ids = agent_ids;
+  a.lk = l_k_pools;
+  a.lv = l_v_pools;
+  a.bk = b_k;
+  a.bv = b_v;
+  a.ranks = ranks;
+  a.out = out;
+  a.counters = (unsigned*)workspace;
+  a.partials = need ? (float*)((char*)workspace + p.counter_bytes) : nullptr;
+  a.max_blocks = max_blocks;
+  a.num_groups = num_groups;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.G = p.G;
+  a.apt = p.apt;
+  a.row_tiles = p.row_tiles;
+  a.split = p.split;
+  a.nsplit = p.nsplit;
+  a.part_stride = p.part_stride;
+  a.n_work = num_groups * p.row_tiles * p.nsplit * Hkv;
+  a.sm_scale = sm_scale;
+  a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.rope = rope_theta > 0.f;
+  a.rope_log2_theta = log2_theta(rope_theta);
+  const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, (hipStream_t)stream)
+                                         : launch_decode_f32(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// --------------------------------------------------------------------------
+size_t lora_attn_prefill_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int32_t d, int32_t max_rank,
+                                        int32_t max_q_len, int32_t max_context_len, int32_t dtype) {
+  (void)S; (void)Hq; (void)Hkv; (void)d; (void)max_rank; (void)max_q_len; (void)max_context_len; (void)dtype;
+  return 0;
+}
+
+int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                      int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                      const int32_t* cu_q_lens, int32_t max_q_len, const int32_t* agent_ids,
+                      const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                      const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
+                      int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
+                      int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_decode_sizes(S, S > 0 ? S : 1, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  if (rc != LRA_OK) return rc;
+  if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "prefill supports LRA_BF16 only");
+  if (S == 0) return ok();
+  if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (N_agents < 1) return fail(LRA_ERR_INVALID_ARG, "N_agents must be >= 1 (got %d)", N_agents);
+  if (max_q_len < 1 || max_q_len > max_context_len)
+    return fail(LRA_ERR_INVALID_ARG, "max_q_len must be in 1..max_context_len (got %d)", max_q_len);
+  if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
+    return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
+  if (!q || !k_base || !v_base || !block_tables || !context_lens || !cu_q_lens || !agent_ids || !l_k_pools ||
+      !l_v_pools || !b_k || !b_v || !ranks || !out)
+    return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+  if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
+    return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
+  if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
+    return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
+  (void)workspace;
+  (void)workspace_bytes;
+  PrefillArgs a{};
+  a.q = q;
+  a.kb = k_base;
+  a.vb = v_base;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.agent_ids = agent_ids;
+  a.lk = l_k_pools;
+  a.lv = l_v_pools;
+  a.bk = b_k;
+  a.bv = b_v;
+  a.ranks = ranks;
+  a.out = out;
+  a.max_blocks = max_blocks;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.G = Hq / Hkv;
+  a.max_q_len = max_q_len;
+  a.rp = pad_rank(max_rank);
+  a.sm_scale = sm_scale;
+  a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.rope = rope_theta > 0.f;
+  a.rope_log2_theta = log2_theta(rope_theta);
+  const hipError_t e = launch_prefill_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,117 @@
+"""The C-ABI library on the host: it loads, exports every symbol the header
+declares, and rejects bad arguments before any HIP call (so these run
+without a GPU). Fake device addresses are never dereferenced: each call
+fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import shared_base_kv_amd as lra
+from shared_base_kv_amd import binding as B
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "lra.h")
+FAKE = 0x10000  # 16-byte aligned, never touched
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", src)) - {"defined"})
+
+
+def test_exports_every_declared_symbol():
+    lib = lra.load()
+    names = _declared()
+    assert set(names) == set(B.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_matches_header():
+    m = re.search(r"#define LRA_VERSION (\d+)", open(HEADER).read())
+    assert lra.lra_version() == int(m.group(1))
+
+
+def _decode(**over):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=512, ctx=FAKE, max_ctx=8192, go=FAKE, ng=1, ag=FAKE,
+                lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8, d=128, bs=16,
+                sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    args.update(over)
+    rc = lra.load().lora_attn_decode(*args.values())
+    return rc, lra.lra_last_error()
+
+
+@pytest.mark.parametrize("over,code,frag", [
+    (dict(q=None), B.LRA_ERR_INVALID_ARG, "null"),
+    (dict(out=None), B.LRA_ERR_INVALID_ARG, "null"),
+    (dict(q=FAKE + 2), B.LRA_ERR_INVALID_ARG, "aligned"),
+    (dict(Hq=30), B.LRA_ERR_INVALID_ARG, "multiple"),
+    (dict(Hq=8 * 17), B.LRA_ERR_UNSUPPORTED, "16 query heads"),
+    (dict(d=64), B.LRA_ERR_UNSUPPORTED, "d = 128"),
+    (dict(dtype=7), B.LRA_ERR_UNSUPPORTED, "dtype"),
+    (dict(max_rank=65), B.LRA_ERR_UNSUPPORTED, "max_rank"),
+    (dict(max_rank=0), B.LRA_ERR_UNSUPPORTED, "max_rank"),
+    (dict(bs=32), B.LRA_ERR_UNSUPPORTED, "block_size"),
+    (dict(max_blocks=10), B.LRA_ERR_INVALID_ARG, "max_blocks"),
+    (dict(ng=5), B.LRA_ERR_INVALID_ARG, "num_groups"),
+    (dict(NA=0), B.LRA_ERR_INVALID_ARG, "N_agents"),
+    (dict(wsb=100), B.LRA_ERR_WORKSPACE, "workspace"),
+    (dict(ws=None), B.LRA_ERR_WORKSPACE, "workspace"),
+    (dict(theta=-1.0), B.LRA_ERR_INVALID_ARG, "rope_theta"),
+    (dict(sc=float("inf")), B.LRA_ERR_INVALID_ARG, "sm_scale"),
+])
+def test_decode_rejects_bad_arguments(over, code, frag):
+    rc, msg = _decode(**over)
+    assert rc == code, msg
+    assert frag in msg
+
+
+def test_empty_batch_is_a_no_op():
+    rc, msg = _decode(S=0)
+    assert rc == B.LRA_OK and msg == ""
+
+
+def test_decode_workspace_is_small_and_bounded():
+    """Workspace holds split partials only: O(splits * rows * (d + r + 4))
+    floats, bounded as the context grows, never O(T * d)."""
+    f = lra.lora_attn_decode_workspace_size
+    small = f(4, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16)
+    assert 0 < small < 8 * 1024 * 1024
+    sizes = [f(8, 1, 32, 8, 128, 64, T, lra.LRA_BF16) for T in (4096, 32768, 1 << 20, 1 << 24)]
+    bound = 8 * 2 * 64 * 16 * (4 + 128 + 64) * 4 + 4096
+    assert max(sizes) <= bound
+    assert sizes[-1] < (1 << 24) * 128 * 2
+    assert lra.lora_attn_decode_counter_bytes(4, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16) % 256 == 0
+    assert f(4, 1, 32, 8, 128, 16, 8192, lra.LRA_F32) == 0  # fp32 path has no split
+    assert f(4, 1, 30, 8, 128, 16, 8192, lra.LRA_BF16) == 0  # invalid sizes -> 0
+
+
+def test_build_rejects_bad_arguments():
+    lib = lra.load()
+    call = lambda **o: lib.lr_cache_build(*dict(dict(X=FAKE, ldx=4096, A=FAKE, lda=16, L=FAKE, ldl=16, slot=None,  # noqa: E731
+                                                     lay=0, n=512, hidden=4096, ncols=16, dtype=lra.LRA_BF16,
+                                                     ws=FAKE, wsb=1 << 30, stream=None), **o).values())
+    assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
+    assert call(X=None) == B.LRA_ERR_INVALID_ARG
+    assert call(hidden=4100, ldx=4100) == B.LRA_ERR_UNSUPPORTED
+    assert call(ncols=300, lda=300, ldl=300) == B.LRA_ERR_UNSUPPORTED
+    assert call(lay=1) == B.LRA_ERR_INVALID_ARG  # rank-major needs a slot mapping
+    assert call(ldl=8) == B.LRA_ERR_INVALID_ARG
+    assert call(wsb=10) == B.LRA_ERR_WORKSPACE
+    assert call(n=0) == B.LRA_OK
+    assert lra.lr_cache_build_workspace_size(512, 4096, 16) == 8 * 512 * 16 * 4
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = lra.load()
+    base = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=600, ctx=FAKE, max_ctx=8704, cu=FAKE, mq=512, ag=FAKE,
+                lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8, d=128, bs=16,
+                sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE, ws=None, wsb=0, stream=None)
+    call = lambda **o: lib.lora_attn_prefill(*dict(base, **o).values())  # noqa: E731
+    assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
+    assert call(cu=None) == B.LRA_ERR_INVALID_ARG
+    assert call(mq=0) == B.LRA_ERR_INVALID_ARG
+    assert call(mq=9000) == B.LRA_ERR_INVALID_ARG
+    assert call(S=0) == B.LRA_OK
