@@ -1,0 +1,436 @@
+#!/usr/bin/env python3
+"""Benchmark of the shared-base + low-rank KV attention hot path on one MI355X.
+
+Prints ONE JSON line. The headline (``value``) is decode tokens/s of the
+8B-shaped single-layer decode (32 q / 8 KV heads, d=128, T=8192, 4 agents
+sharing one base and one shared-A r=16 low-rank cache, rotary theta 5e5,
+shuffled 16-token blocks, bf16): one step = one lora_attn_decode call
+serving the 4 agents' decode tokens. Inputs are resident in HBM before the
+timed region; the base and low-rank pools are rotated over enough copies to
+exceed the 256 MB last-level cache, so every step streams from HBM.
+
+``roofline`` is for the decode kernel: algorithmic bytes per launch (each
+distinct buffer once: base K/V, shared L_k/L_v, the 4 agents' B_k/B_v, q,
+out, block table) divided by the kernel's mean duration from HIP events
+around each launch in the timed region. ``traffic`` comes from the committed
+rocprofv3 counter summary when it was taken on the current kernel source.
+
+Other legs (same JSON line, under "legs"): the prefill chunk with its
+low-rank cache build, the 32-layer long-context decode, the 64-request
+serving mix and the tiny fp32 decode. ``cpu_baseline`` times the fp64
+oracle on the host on a bounded sample of the headline workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+MALL_BYTES = 256 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- timing
+def _timed(launch, K, W, n_copies):
+    """Run W untimed then exactly K timed launches (launch(i) uses copy
+    i % n_copies). The GPU is kept busy with a spin kernel while the host
+    enqueues, so the K launches run back to back and HIP events around each
+    one measure the kernel, not host overhead. Returns (step_ms, kernel_ms)."""
+    import torch
+
+    for i in range(W):
+        launch(i % n_copies)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e6) + K * 200000)
+    t0.record()
+    for i in range(K):
+        starts[i].record()
+        launch(i % n_copies)
+        ends[i].record()
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / K
+    kern = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
+    return step_ms, sum(kern) / K, kern[len(kern) // 2]
+
+
+def _decode_caller(dw, ws_bytes):
+    """Pre-marshalled C call of lora_attn_decode for each pool copy."""
+    import torch
+
+    import shared_base_kv_amd as lra
+
+    lib = lra.load()
+    w = dw.w
+    ws = torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device="cuda")
+    out = dw.new_out()
+    ng = dw.group_offsets.numel() - 1
+    code = lra.LRA_BF16 if w.dtype == "bf16" else lra.LRA_F32
+    stream = torch.cuda.current_stream().cuda_stream
+    copies = dw.copies if hasattr(dw, "copies") else [(dw.k_base, dw.v_base, dw.lk_ptrs, dw.lv_ptrs)]
+    argsets = []
+    for kb, vb, lkp, lvp in copies:
+        argsets.append((dw.q.data_ptr(), kb.data_ptr(), vb.data_ptr(), dw.block_tables.data_ptr(),
+                        dw.block_tables.shape[1], dw.context_lens.data_ptr(), dw.max_context_len,
+                        dw.group_offsets.data_ptr(), ng, dw.agent_ids.data_ptr(), lkp.data_ptr(), lvp.data_ptr(),
+                        dw.bk_ptrs.data_ptr(), dw.bv_ptrs.data_ptr(), dw.ranks.data_ptr(), dw.max_rank, w.S,
+                        w.n_agents, w.Hq, w.Hkv, w.d, 16, w.sm_scale, w.theta, code, out.data_ptr(),
+                        ws.data_ptr(), ws.numel(), stream))
+
+    def launch(i):
+        rc = lib.lora_attn_decode(*argsets[i])
+        if rc:
+            raise lra.LraError(rc, lra.lra_last_error())
+
+    return launch, out, ws, len(argsets)
+
+
+def _replicate(dw, min_bytes):
+    """Extra device copies of the base and low-rank pools so the rotation
+    over copies exceeds the last-level cache."""
+    import torch
+
+    per = dw.k_base.nbytes + dw.v_base.nbytes + sum(t.nbytes for t in dw.lk_pools + dw.lv_pools)
+    n = max(1, -(-min_bytes // per))
+    copies = [(dw.k_base, dw.v_base, dw.lk_ptrs, dw.lv_ptrs)]
+    keep = []
+    for _ in range(n - 1):
+        kb, vb = dw.k_base.clone(), dw.v_base.clone()
+        lks = [t.clone() for t in dw.lk_pools]
+        lvs = [t.clone() for t in dw.lv_pools]
+        w = dw.w
+        lkp = torch.tensor([lks[w.pool_of_agent[a]].data_ptr() for a in range(w.n_agents)], dtype=torch.int64,
+                           device="cuda")
+        lvp = torch.tensor([lvs[w.pool_of_agent[a]].data_ptr() for a in range(w.n_agents)], dtype=torch.int64,
+                           device="cuda")
+        keep += [lks, lvs]
+        copies.append((kb, vb, lkp, lvp))
+    dw.copies = copies
+    dw._keep = keep
+    return n
+
+
+def decode_bytes(w):
+    """Algorithmic bytes of one decode step: every distinct buffer once."""
+    es = 2 if w.dtype == "bf16" else 4
+    tok_groups = sum(w.segments[i].T for i in range(len(w.segments)))
+    base = tok_groups * w.Hkv * w.d * es * 2
+    lr = sum(w.segments[i].T * sum(w.pool_rank[p] for p in w.segments[i].pools) for i in range(len(w.segments))) * es * 2
+    used_agents = sorted({sq.agent for sq in w.seqs})
+    bmat = sum(w.ranks[a] * w.Hkv * w.d * es * 2 for a in used_agents)
+    qo = w.S * w.Hq * w.d * es * 2
+    tables = sum(-(-w.context_len(s) // 16) for s in range(w.S)) * 4 + w.S * 4 * 2
+    return base + lr + bmat + qo + tables
+
+
+def decode_flops(w):
+    """Algorithmic FLOPs of one decode step over visible pairs: adapter key
+    rebuild, QK, PV, P L_v and the final C B_v."""
+    G = w.Hq // w.Hkv
+    f = 0
+    for s in range(w.S):
+        T = w.context_len(s)
+        r = w.ranks[w.seqs[s].agent]
+        f += 2 * T * r * w.Hkv * w.d  # rebuild L_k B_k (per agent, per KV head)
+        f += 2 * T * w.Hq * w.d * 2  # QK and PV
+        f += 2 * T * w.Hq * r  # P L_v
+        f += 2 * w.Hq * r * w.d  # C B_v
+    return f
+
+
+def _traffic(kernel_src, launches_per_step=1):
+    """HBM bytes per launch from the committed counter summary, or None if it
+    was taken on another version of the kernel source."""
+    path = os.path.join(PROFILES, "decode_8b_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(os.path.join(ROOT, "shared_base_kv_amd", "csrc", kernel_src), "rb").read()).hexdigest()
+    if rec.get("kernel_source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ------------------------------------------------------------------ legs
+def leg_decode(K, W):
+    from workloads import config_8b_decode
+    from workloads.device import upload
+
+    import shared_base_kv_amd as lra
+
+    w = config_8b_decode()
+    dw = upload(w)
+    ncopy = _replicate(dw, 2 * MALL_BYTES)
+    wsb = lra.lora_attn_decode_workspace_size(w.S, 1, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len, lra.LRA_BF16)
+    launch, _, _, n = _decode_caller(dw, wsb)
+    step_ms, kern_ms, kern_med = _timed(launch, K, W, n)
+    nbytes = decode_bytes(w)
+    return dict(w=w, step_ms=step_ms, kernel_ms=kern_ms, kernel_median_ms=kern_med, bytes=nbytes,
+                flops=decode_flops(w), tokens=w.S, copies=ncopy)
+
+
+def leg_long(K, W):
+    """32-layer long-context decode: 32 independent layer calls per step."""
+    import concurrent.futures as cf
+
+    import torch
+
+    import shared_base_kv_amd as lra
+    from workloads import config_long_layer
+    from workloads.device import upload
+
+    layers = [config_long_layer(i) for i in range(32)]
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        pools = list(ex.map(lambda w: w.host_pools(), layers))
+    dws = []
+    for i in range(len(layers)):
+        dws.append(upload(layers[i], host_pools=pools[i]))
+        pools[i] = None
+    wsb = lra.lora_attn_decode_workspace_size(8, 1, 32, 8, 128, 64, 32768, lra.LRA_BF16)
+    calls = [_decode_caller(dw, wsb) for dw in dws]
+
+    def launch(i):
+        for c in calls:
+            c[0](0)
+
+    step_ms, kern_ms, kern_med = _timed(launch, max(2, K // 8), min(W, 2), 1)
+    nbytes = sum(decode_bytes(w) for w in layers)
+    flops = sum(decode_flops(w) for w in layers)
+    del dws, calls
+    torch.cuda.empty_cache()
+    return dict(step_ms=step_ms, layer_ms=kern_ms / 32, bytes=nbytes, flops=flops, tokens=8)
+
+
+def leg_mix(K, W):
+    import torch
+
+    import shared_base_kv_amd as lra
+    from workloads import config_serving_mix
+    from workloads.device import upload
+
+    w = config_serving_mix()
+    dw = upload(w)
+    wsb = lra.lora_attn_decode_workspace_size(w.S, w.S, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len,
+                                              lra.LRA_BF16)
+    launch, _, _, n = _decode_caller(dw, wsb)
+    step_ms, kern_ms, kern_med = _timed(launch, max(4, K // 4), W, n)
+    out = dict(step_ms=step_ms, kernel_ms=kern_ms, bytes=decode_bytes(w), flops=decode_flops(w), tokens=w.S,
+               total_context=int(sum(w.context_len(s) for s in range(w.S))))
+    del dw
+    torch.cuda.empty_cache()
+    return out
+
+
+def leg_tiny(K, W):
+    import shared_base_kv_amd as lra
+    from workloads import config_tiny_f32
+    from workloads.device import upload
+
+    w = config_tiny_f32()
+    dw = upload(w)
+    launch, _, _, n = _decode_caller(dw, 0)
+    step_ms, kern_ms, _ = _timed(launch, K, W, n)
+    return dict(step_ms=step_ms, kernel_ms=kern_ms, tokens=w.S)
+
+
+def leg_prefill(K, W):
+    """Prefill chunk: lr_cache_build for the 4 agents' new tokens (X_a A_k and
+    X_a A_v into the paged pools), then lora_attn_prefill."""
+    import torch
+
+    import shared_base_kv_amd as lra
+    from workloads import bf16_bits, build_inputs, config_prefill
+    from workloads.device import upload
+
+    w = config_prefill()
+    dw = upload(w)
+    # build inputs: X_a [512, 4096] per agent, A_k and A_v [4096, 16]
+    dev = lambda x: torch.from_numpy(bf16_bits(x).view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
+    Xs = [dev(build_inputs(512, 4096, 16, seed=100 + a)[0]) for a in range(4)]
+    Ak = dev(build_inputs(1, 4096, 16, seed=200)[1])
+    Av = dev(build_inputs(1, 4096, 16, seed=201)[1])
+    slots = []
+    for a in range(4):
+        seg = w.segments[1 + a]
+        ids = torch.from_numpy(seg.blocks.astype("int64"))
+        slots.append((ids[:, None] * 16 + torch.arange(16)[None, :]).reshape(-1)[: seg.T].cuda())
+    bws = torch.empty(lra.lr_cache_build_workspace_size(512, 4096, 16), dtype=torch.uint8, device="cuda")
+    out = dw.new_out()
+
+    def build_all():
+        for a in range(4):
+            lra.lr_cache_build(Xs[a], Ak, dw.lk_pools[0], bws, slot_mapping=slots[a], l_layout=lra.LRA_L_TOKEN_MAJOR,
+                               ldl=16)
+            lra.lr_cache_build(Xs[a], Av, dw.lv_pools[0], bws, slot_mapping=slots[a], l_layout=lra.LRA_L_RANK_MAJOR)
+
+    def prefill():
+        lra.lora_attn_prefill(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
+                              dw.cu_q_lens, dw.max_q_len, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs,
+                              dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out)
+
+    kk = max(4, K // 5)
+    b_step, b_kern, _ = _timed(lambda i: build_all(), kk, 2, 1)
+    p_step, p_kern, p_med = _timed(lambda i: prefill(), kk, 2, 1)
+    flops = prefill_flops(w)
+    return dict(build_ms=b_kern, prefill_ms=p_kern, prefill_median_ms=p_med, flops=flops,
+                tokens=sum(sq.q_len for sq in w.seqs), build_bytes=4 * 2 * (512 * 4096 * 2 + 4096 * 16 * 2 + 512 * 16 * 2))
+
+
+def prefill_flops(w):
+    """Visible-pair FLOPs of the prefill chunk: QK, PV, P L_v over causal pairs,
+    the adapter key rebuild once per token, and C B_v per row."""
+    G = w.Hq // w.Hkv
+    f = 0
+    for s, sq in enumerate(w.seqs):
+        T = w.context_len(s)
+        r = w.ranks[sq.agent]
+        nq = sq.q_len
+        pairs = sum(T - nq + i + 1 for i in range(nq))
+        f += pairs * w.Hq * (2 * w.d * 2 + 2 * r)
+        f += 2 * T * r * w.Hkv * w.d
+        f += 2 * nq * w.Hq * r * w.d
+    return f
+
+
+# ------------------------------------------------------------- baseline
+def cpu_baseline(seconds):
+    import numpy as np
+
+    import oracle
+    from workloads import config_8b_decode
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        threads = 1
+    w = config_8b_decode()
+    logical = [w.logical(s) for s in range(w.S)]
+    done = 0
+    t0 = time.perf_counter()
+    while True:
+        for lg in logical:
+            oracle.lora_attention(**lg, sm_scale=w.sm_scale, theta=w.theta)
+            done += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle on the 8B-shaped decode workload: {done} sequence decodes "
+                      f"({done // w.S} full 4-agent steps) in {dt:.1f} s, BLAS threads={threads}, "
+                      f"host cpus={len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    args = _args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(DESIGN.md describes how it would shard). Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    torch.cuda.set_device(0)
+    legs = set(args.legs.split(","))
+    K, W = args.steps, args.warmup
+
+    torch.cuda.synchronize()
+    log = lambda m: print(f"[bench] {m}", file=sys.stderr, flush=True)  # noqa: E731
+    head = leg_decode(K, W)
+    log(f"decode leg done: {head['kernel_ms'] * 1e3:.2f} us/launch")
+    w = head["w"]
+    step_s = head["step_ms"] / 1e3
+    kern_s = head["kernel_ms"] / 1e3
+    achieved = head["bytes"] / kern_s / 1e9
+    traffic = _traffic("decode_bf16.hip")
+    res = {
+        "metric": "LoRA-attn decode tokens/s (8B-shaped layer, 4 agents, shared base, T=8192)",
+        "value": round(head["tokens"] / step_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(head["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) base/low-rank caches, N(0,0.1/sqrt(r)) adapters)",
+        "config": {"workload": "8b_decode_shared_base", "Hq": 32, "Hkv": 8, "head_dim": 128, "context": 8192,
+                   "agents": 4, "rank": 16, "shared_a": True, "rope_theta": 5e5, "block_size": 16,
+                   "pool_copies_rotated": head["copies"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "decode_bf16_kernel<16>", "algorithmic_bytes_per_launch": head["bytes"],
+                     "kernel_ms_mean": round(head["kernel_ms"], 5),
+                     "kernel_ms_median": round(head["kernel_median_ms"], 5)},
+    }
+    extra = {}
+    if "prefill" in legs:
+        try:
+            p = leg_prefill(K, W)
+            tf = p["flops"] / (p["prefill_ms"] / 1e3) / 1e12
+            extra["prefill_chunk"] = {
+                "prefill_tokens_per_s": round(p["tokens"] / (p["prefill_ms"] / 1e3), 1),
+                "prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
+                "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                             "frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": p["flops"]},
+                "lr_cache_build_ms_8_calls": round(p["build_ms"], 4),
+                "lr_cache_build_GBps": round(p["build_bytes"] / (p["build_ms"] / 1e3) / 1e9, 1),
+            }
+        except Exception as e:  # prefill not available
+            extra["prefill_chunk"] = {"error": str(e)[:200]}
+        log("prefill leg done")
+    if "long" in legs:
+        lo = leg_long(K, W)
+        extra["long_ctx_32_layers"] = {
+            "tokens_per_s": round(lo["tokens"] / (lo["step_ms"] / 1e3), 1), "ms_per_step": round(lo["step_ms"], 4),
+            "GBps": round(lo["bytes"] / (lo["step_ms"] / 1e3) / 1e9, 1),
+            "hbm_frac": round(lo["bytes"] / (lo["step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tflops": round(lo["flops"] / (lo["step_ms"] / 1e3) / 1e12, 2), "bytes_per_step": lo["bytes"]}
+        log("long-context leg done")
+    if "mix" in legs:
+        mx = leg_mix(K, W)
+        extra["serving_mix_64"] = {
+            "tokens_per_s": round(mx["tokens"] / (mx["step_ms"] / 1e3), 1), "ms_per_step": round(mx["step_ms"], 4),
+            "kernel_ms": round(mx["kernel_ms"], 4),
+            "GBps": round(mx["bytes"] / (mx["kernel_ms"] / 1e3) / 1e9, 1),
+            "hbm_frac": round(mx["bytes"] / (mx["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "bytes_per_step": mx["bytes"], "total_context": mx["total_context"]}
+        log("serving-mix leg done")
+    if "tiny" in legs:
+        ti = leg_tiny(K, W)
+        extra["tiny_f32"] = {"us_per_step": round(ti["step_ms"] * 1e3, 2), "kernel_us": round(ti["kernel_ms"] * 1e3, 2)}
+    res["legs"] = extra
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -19,7 +19,7 @@ def dtype_code(w):
 
 def decode_workspace(dw):
     w = dw.w
-    ng = len(w.group_offsets) - 1
+    ng = dw.group_offsets.numel() - 1 if dw.group_offsets is not None else w.S
     n = lra.lora_attn_decode_workspace_size(w.S, ng, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len, dtype_code(w))
     return torch.zeros(max(n, 256), dtype=torch.uint8, device=dw.q.device)
 

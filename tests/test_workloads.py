@@ -5,6 +5,7 @@ import numpy as np
 import torch
 
 from workloads import BLOCK, bf16_bits, decode_workload, prefill_workload, round_bf16
+from workloads.synth import _bits_rne
 
 
 def test_round_bf16_matches_torch_rne():
@@ -15,6 +16,8 @@ def test_round_bf16_matches_torch_rne():
     got = round_bf16(x)
     assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
     assert np.array_equal(bf16_bits(got), torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+    fin = np.isfinite(x)
+    assert np.array_equal(_bits_rne(x[fin].copy()), bf16_bits(got[fin]))
 
 
 def _gather_check(w, poison):

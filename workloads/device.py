@@ -55,9 +55,9 @@ class DeviceWorkload:
         return torch.empty(self.q.shape, dtype=self.torch_dtype, device=self.q.device)
 
 
-def upload(w: Workload, device="cuda", poison: bool = False) -> DeviceWorkload:
+def upload(w: Workload, device="cuda", poison: bool = False, host_pools=None) -> DeviceWorkload:
     dev = torch.device(device)
-    kpool, vpool, lkp, lvp = w.host_pools(poison=poison)
+    kpool, vpool, lkp, lvp = host_pools if host_pools is not None else w.host_pools(poison=poison)
     conv = _u16 if w.dtype == "bf16" else (lambda x: x)
     k_base = _t(conv(kpool), dev, w.dtype)
     v_base = _t(conv(vpool), dev, w.dtype)

@@ -27,7 +27,9 @@ Layouts handed to the library (block size 16):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -53,11 +55,29 @@ def bf16_bits(x_rounded: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(x_rounded, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def _normal(rng: np.random.Generator, shape, sigma: float, dtype: str) -> np.ndarray:
+def _bits_rne(x: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (round to nearest even) of finite float32 draws, in place."""
+    u = x.view(np.uint32)
+    t = u >> 16
+    t &= 1
+    t += np.uint32(0x7FFF)
+    t += u
+    t >>= 16
+    return t.astype(np.uint16)
+
+
+def _normal(rng: np.random.Generator, shape, sigma: float, dtype: str, bits: bool = False) -> np.ndarray:
+    """N(0, sigma) draws as float32; bf16 workloads round once to bf16.
+    With ``bits`` a bf16 draw is returned as its uint16 bit pattern."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
     if sigma != 1.0:
         x *= np.float32(sigma)
-    return round_bf16(x) if dtype == "bf16" else x
+    if dtype != "bf16":
+        return x
+    b = _bits_rne(x)
+    if bits:
+        return b
+    return (b.astype(np.uint32) << 16).view(np.float32)
 
 
 @dataclass
@@ -154,16 +174,17 @@ class Workload:
             self._cache[key] = (bk, bv)
         return self._cache[key]
 
-    def segment_data(self, sid: int):
-        """Logical rows of one segment: kb, vb [T, Hkv, d]; lk, lv: {pool: [T, r]}."""
+    def segment_data(self, sid: int, bits: bool = False):
+        """Logical rows of one segment: kb, vb [T, Hkv, d]; lk, lv: {pool: [T, r]}.
+        With ``bits`` (bf16 only) the arrays hold uint16 bit patterns."""
         seg = self.segments[sid]
         rng = np.random.default_rng(seg.seed)
-        kb = _normal(rng, (seg.T, self.Hkv, self.d), 1.0, self.dtype)
-        vb = _normal(rng, (seg.T, self.Hkv, self.d), 1.0, self.dtype)
+        kb = _normal(rng, (seg.T, self.Hkv, self.d), 1.0, self.dtype, bits)
+        vb = _normal(rng, (seg.T, self.Hkv, self.d), 1.0, self.dtype, bits)
         lk, lv = {}, {}
         for p in seg.pools:
-            lk[p] = _normal(rng, (seg.T, self.pool_rank[p]), 1.0, self.dtype)
-            lv[p] = _normal(rng, (seg.T, self.pool_rank[p]), 1.0, self.dtype)
+            lk[p] = _normal(rng, (seg.T, self.pool_rank[p]), 1.0, self.dtype, bits)
+            lv[p] = _normal(rng, (seg.T, self.pool_rank[p]), 1.0, self.dtype, bits)
         return kb, vb, lk, lv
 
     def q_offsets(self) -> np.ndarray:
@@ -206,9 +227,11 @@ class Workload:
         vpool = np.full((nb, H, d, BLOCK), fill, dtype=st)
         lkp = [np.full((nb, BLOCK, r), fill, dtype=st) for r in self.pool_rank]
         lvp = [np.full((nb, r, BLOCK), fill, dtype=st) for r in self.pool_rank]
-        conv = bf16_bits if st == np.uint16 else (lambda x: x)
-        for sid, seg in enumerate(self.segments):
-            kb, vb, lk, lv = self.segment_data(sid)
+        bits = st == np.uint16
+
+        def fill_segment(sid):
+            seg = self.segments[sid]
+            kb, vb, lk, lv = self.segment_data(sid, bits=bits)
             nfull = seg.T // BLOCK
             rem = seg.T - nfull * BLOCK
             pad = (-seg.T) % BLOCK
@@ -218,8 +241,8 @@ class Workload:
                     x = np.concatenate([x, np.zeros((pad,) + x.shape[1:], x.dtype)])
                 return x.reshape((-1, BLOCK) + x.shape[1:])
 
-            kbb = conv(blocks_of(kb)).transpose(0, 2, 1, 3)  # [nblk, H, 16, d]
-            vbb = conv(blocks_of(vb)).transpose(0, 2, 3, 1)  # [nblk, H, d, 16]
+            kbb = blocks_of(kb).transpose(0, 2, 1, 3)  # [nblk, H, 16, d]
+            vbb = blocks_of(vb).transpose(0, 2, 3, 1)  # [nblk, H, d, 16]
             ids = seg.blocks
             if nfull:
                 kpool[ids[:nfull]] = kbb[:nfull]
@@ -228,14 +251,19 @@ class Workload:
                 kpool[ids[nfull], :, :rem, :] = kbb[nfull, :, :rem, :]
                 vpool[ids[nfull], :, :, :rem] = vbb[nfull, :, :, :rem]
             for p in seg.pools:
-                lkb = conv(blocks_of(lk[p]))  # [nblk, 16, r]
-                lvb = conv(blocks_of(lv[p])).transpose(0, 2, 1)  # [nblk, r, 16]
+                lkb = blocks_of(lk[p])  # [nblk, 16, r]
+                lvb = blocks_of(lv[p]).transpose(0, 2, 1)  # [nblk, r, 16]
                 if nfull:
                     lkp[p][ids[:nfull]] = lkb[:nfull]
                     lvp[p][ids[:nfull]] = lvb[:nfull]
                 if rem:
                     lkp[p][ids[nfull], :rem, :] = lkb[nfull, :rem, :]
                     lvp[p][ids[nfull], :, :rem] = lvb[nfull, :, :rem]
+
+        # segments own disjoint blocks, so they fill in parallel
+        workers = max(1, min(16, len(os.sched_getaffinity(0)), len(self.segments)))
+        with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill_segment, range(len(self.segments))))
         return kpool, vpool, lkp, lvp
 
     def host_adapters(self):
