@@ -52,30 +52,26 @@ def _args():
 # ---------------------------------------------------------------- timing
 def _timed(launch, K, W, n_copies):
     """Run W untimed then exactly K timed launches (launch(i) uses copy
-    i % n_copies). The GPU is kept busy with a spin kernel while the host
-    enqueues, so the K launches run back to back and HIP events around each
-    one measure the kernel, not host overhead. Returns (step_ms, kernel_ms)."""
+    i % n_copies), back to back between two HIP events on the launch stream.
+    The GPU is kept busy with a spin kernel while the host enqueues, so the K
+    launches run back to back and the event interval holds GPU time only.
+    Returns the mean time per launch in ms (kernel time plus the gap
+    between dependent launches; no per-launch event overhead)."""
     import torch
 
     for i in range(W):
         launch(i % n_copies)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(int(2e6) + K * 200000)
     t0.record()
     for i in range(K):
-        starts[i].record()
         launch(i % n_copies)
-        ends[i].record()
     t1.record()
     torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / K
-    kern = sorted(s.elapsed_time(e) for s, e in zip(starts, ends))
-    return step_ms, sum(kern) / K, kern[len(kern) // 2]
+    return t0.elapsed_time(t1) / K
 
 
 def _decode_caller(dw, ws_bytes):
@@ -187,10 +183,10 @@ def leg_decode(K, W):
     ncopy = _replicate(dw, 2 * MALL_BYTES)
     wsb = lra.lora_attn_decode_workspace_size(w.S, 1, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len, lra.LRA_BF16)
     launch, _, _, n = _decode_caller(dw, wsb)
-    step_ms, kern_ms, kern_med = _timed(launch, K, W, n)
+    step_ms = _timed(launch, K, W, n)
     nbytes = decode_bytes(w)
-    return dict(w=w, step_ms=step_ms, kernel_ms=kern_ms, kernel_median_ms=kern_med, bytes=nbytes,
-                flops=decode_flops(w), tokens=w.S, copies=ncopy)
+    return dict(w=w, step_ms=step_ms, kernel_ms=step_ms, bytes=nbytes, flops=decode_flops(w), tokens=w.S,
+                copies=ncopy)
 
 
 def leg_long(K, W):
@@ -217,12 +213,12 @@ def leg_long(K, W):
         for c in calls:
             c[0](0)
 
-    step_ms, kern_ms, kern_med = _timed(launch, max(2, K // 8), min(W, 2), 1)
+    step_ms = _timed(launch, max(2, K // 8), min(W, 2), 1)
     nbytes = sum(decode_bytes(w) for w in layers)
     flops = sum(decode_flops(w) for w in layers)
     del dws, calls
     torch.cuda.empty_cache()
-    return dict(step_ms=step_ms, layer_ms=kern_ms / 32, bytes=nbytes, flops=flops, tokens=8)
+    return dict(step_ms=step_ms, layer_ms=step_ms / 32, bytes=nbytes, flops=flops, tokens=8)
 
 
 def leg_mix(K, W):
@@ -237,8 +233,8 @@ def leg_mix(K, W):
     wsb = lra.lora_attn_decode_workspace_size(w.S, w.S, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len,
                                               lra.LRA_BF16)
     launch, _, _, n = _decode_caller(dw, wsb)
-    step_ms, kern_ms, kern_med = _timed(launch, max(4, K // 4), W, n)
-    out = dict(step_ms=step_ms, kernel_ms=kern_ms, bytes=decode_bytes(w), flops=decode_flops(w), tokens=w.S,
+    step_ms = _timed(launch, max(4, K // 4), W, n)
+    out = dict(step_ms=step_ms, kernel_ms=step_ms, bytes=decode_bytes(w), flops=decode_flops(w), tokens=w.S,
                total_context=int(sum(w.context_len(s) for s in range(w.S))))
     del dw
     torch.cuda.empty_cache()
@@ -253,8 +249,8 @@ def leg_tiny(K, W):
     w = config_tiny_f32()
     dw = upload(w)
     launch, _, _, n = _decode_caller(dw, 0)
-    step_ms, kern_ms, _ = _timed(launch, K, W, n)
-    return dict(step_ms=step_ms, kernel_ms=kern_ms, tokens=w.S)
+    step_ms = _timed(launch, K, W, n)
+    return dict(step_ms=step_ms, kernel_ms=step_ms, tokens=w.S)
 
 
 def leg_prefill(K, W):
@@ -293,10 +289,10 @@ def leg_prefill(K, W):
                               dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out)
 
     kk = max(4, K // 5)
-    b_step, b_kern, _ = _timed(lambda i: build_all(), kk, 2, 1)
-    p_step, p_kern, p_med = _timed(lambda i: prefill(), kk, 2, 1)
+    b_kern = _timed(lambda i: build_all(), kk, 2, 1)
+    p_kern = _timed(lambda i: prefill(), kk, 2, 1)
     flops = prefill_flops(w)
-    return dict(build_ms=b_kern, prefill_ms=p_kern, prefill_median_ms=p_med, flops=flops,
+    return dict(build_ms=b_kern, prefill_ms=p_kern, flops=flops,
                 tokens=sum(sq.q_len for sq in w.seqs), build_bytes=4 * 2 * (512 * 4096 * 2 + 4096 * 16 * 2 + 512 * 16 * 2))
 
 
@@ -387,8 +383,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_bf16_kernel<16>", "algorithmic_bytes_per_launch": head["bytes"],
-                     "kernel_ms_mean": round(head["kernel_ms"], 5),
-                     "kernel_ms_median": round(head["kernel_median_ms"], 5)},
+                     "ms_per_launch": round(head["kernel_ms"], 5)},
     }
     extra = {}
     if "prefill" in legs:

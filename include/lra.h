@@ -132,17 +132,18 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
  *   rope_theta    rotary base for the adapter key term; 0 disables it.
  *   dtype         LRA_BF16 (split-K kernel on bf16 MFMA, fp32 accumulate) or
  *                 LRA_F32 (fp32 throughout).
- *   workspace     at least lora_attn_decode_workspace_size(...) bytes. Its
- *                 first lora_attn_decode_counter_bytes(...) bytes are arrival
- *                 counters that must be zero before the first call; every
- *                 call leaves them zero again, so a workspace can be reused
- *                 by later calls on the same stream. Calls that overlap in
- *                 time must use different workspaces.
+ *   workspace     at least lora_attn_decode_workspace_size(...) bytes of
+ *                 device memory, 16-byte aligned; it holds fp32 split-K
+ *                 partial states (per split and query row: max, sum and the
+ *                 value accumulator with the adapter term already applied),
+ *                 never a full-dimension adapter key or value. Its contents
+ *                 on entry do not matter. Calls that overlap in time must use
+ *                 different workspaces. May be NULL when the size is 0.
+ *   A call with bf16 is one main kernel, plus a combine kernel when a context
+ *   is split; with f32 it is one kernel.
  * ---------------------------------------------------------------------- */
 size_t lora_attn_decode_workspace_size(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
                                        int32_t max_rank, int32_t max_context_len, int32_t dtype);
-size_t lora_attn_decode_counter_bytes(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
-                                      int32_t max_rank, int32_t max_context_len, int32_t dtype);
 
 int lora_attn_decode(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
                      int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,

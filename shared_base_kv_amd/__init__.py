@@ -12,7 +12,6 @@ from .binding import (  # noqa: F401
     LraError,
     load,
     lora_attn_decode,
-    lora_attn_decode_counter_bytes,
     lora_attn_decode_workspace_size,
     lora_attn_prefill,
     lora_attn_prefill_workspace_size,

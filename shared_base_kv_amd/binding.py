@@ -30,7 +30,6 @@ EXPORTS = (
     "lr_cache_build_workspace_size",
     "lr_cache_build",
     "lora_attn_decode_workspace_size",
-    "lora_attn_decode_counter_bytes",
     "lora_attn_decode",
     "lora_attn_prefill_workspace_size",
     "lora_attn_prefill",
@@ -69,8 +68,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     size8 = [_i32] * 8
     lib.lora_attn_decode_workspace_size.restype = _sz
     lib.lora_attn_decode_workspace_size.argtypes = size8
-    lib.lora_attn_decode_counter_bytes.restype = _sz
-    lib.lora_attn_decode_counter_bytes.argtypes = size8
     attn = [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
             _i32, _i32, _i32, _i32, _f32, _f32, _i32, _p, _p, _sz, _p]
     lib.lora_attn_decode.restype = ctypes.c_int
@@ -143,10 +140,6 @@ def lr_cache_build(X, A, L, workspace, *, slot_mapping=None, l_layout=LRA_L_TOKE
 
 def lora_attn_decode_workspace_size(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) -> int:
     return load().lora_attn_decode_workspace_size(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype)
-
-
-def lora_attn_decode_counter_bytes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) -> int:
-    return load().lora_attn_decode_counter_bytes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype)
 
 
 def lora_attn_decode(q, k_base, v_base, block_tables, context_lens, max_context_len, group_offsets, agent_ids,

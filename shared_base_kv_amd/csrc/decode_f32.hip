@@ -36,6 +36,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
   __shared__ float sM[16], sL[16], sAlpha[16];
   __shared__ float sC[16][64];
   __shared__ int sPhys[kChunk / kBlock];
+  __shared__ double sRev[kMaxRopePairs];
 
   const int s = blockIdx.x / a.Hkv;
   const int h = blockIdx.x % a.Hkv;
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     const int row = e / D, i = e % D;
     sQ[row][i] = ((const float*)a.q)[((size_t)s * a.Hq + h * G + row) * D + i];
   }
+  if (tid < kMaxRopePairs) sRev[tid] = a.rope_rev[tid];
   if (tid < 16) {
     sM[tid] = -INFINITY;
     sL[tid] = 0.f;
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
           x2 = fmaf(l, bk[(size_t)k * HD + h * D + i + HALF], x2);
         }
         if (a.rope) {
-          const double x = (double)n * (exp2(-2.0 * i / D * a.rope_log2_theta) * 0.15915494309189535);
+          const double x = (double)n * sRev[i];
           const float f = (float)(x - __builtin_floor(x));
           const float c = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
           const float y1 = x1 * c - x2 * sn, y2 = x2 * c + x1 * sn;

@@ -45,9 +45,38 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d)
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(((uint32_t)v) << 16); }
 
 // Plain global loads of raw bits (vector loads; never the scalar data cache
-// for writes anywhere in this library).
-__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
-__device__ __forceinline__ uint2 ld8(const void* p) { return *reinterpret_cast<const uint2*>(p); }
+// for writes anywhere in this library). The pointer is taken as a global
+// (address space 1) pointer so no flat access is emitted.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  return __builtin_bit_cast(uint4, *(__attribute__((address_space(1))) const u32x4_t*)(p));
+}
+__device__ __forceinline__ uint2 ld8(const void* p) {
+  return __builtin_bit_cast(uint2, *(__attribute__((address_space(1))) const u32x2_t*)(p));
+}
+__device__ __forceinline__ float4 ldf4(const float* p) {
+  return __builtin_bit_cast(float4, *(__attribute__((address_space(1))) const f32x4*)(p));
+}
+__device__ __forceinline__ float2 ldf2(const float* p) {
+  return __builtin_bit_cast(float2, *(__attribute__((address_space(1))) const f32x2_t*)(p));
+}
+
+// Buffer resources: a raw buffer load whose byte offset is at or past the
+// resource's byte count returns zero without a memory access, so masked
+// lanes take kOob instead of a branch.
+constexpr int kOob = 0x7ffffff0;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bld16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ float wave_max_across_groups(float v) {
   // Reduce over the 4 lane groups (lanes l, l^16, l^32, l^48) that hold the

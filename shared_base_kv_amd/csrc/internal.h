@@ -11,9 +11,11 @@ namespace lra {
 constexpr int kBlock = 16;       // tokens per cache block
 constexpr int kNumCU = 256;      // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXcd = 8;       // workgroups are dealt round-robin over XCDs
-constexpr int kDecodeWaves = 4;  // waves per decode workgroup
+constexpr int kDecodeWaves = 8;  // waves per decode workgroup
 constexpr int kStepTokens = 32;  // tokens per wave step (two cache blocks)
 constexpr int kMaxSplits = 64;   // split-K partitions per (group, head, row tile)
+constexpr int kMaxRopePairs = 64;
+constexpr int kMaxSplitBlocks = 256;  // cache blocks in one split (split <= 4096 tokens)
 
 // Decode launch plan: derived on the host from sizes only, so the workspace
 // query and the launch agree.
@@ -24,8 +26,7 @@ struct DecodePlan {
   int rp;           // rank padded to the MFMA k granule (16, 32, 64)
   int split;        // tokens per split (multiple of kDecodeWaves * kStepTokens)
   int nsplit;       // splits for the longest context
-  int part_stride;  // floats per partial row: 4 (m, l, pad) + d + rp
-  size_t counter_bytes;
+  int part_stride;  // floats per partial row record: 4 (m, l, seq, nact) + d
   size_t partial_bytes;
 };
 
@@ -43,7 +44,6 @@ struct DecodeArgs {
   const void* const* bv;
   const int32_t* ranks;
   void* out;
-  unsigned* counters;
   float* partials;
   int32_t max_blocks;
   int32_t num_groups;
@@ -60,8 +60,9 @@ struct DecodeArgs {
   int32_t n_work;  // num_groups * row_tiles * nsplit * Hkv
   float sm_scale;
   float sm_scale_log2;  // sm_scale * log2(e)
+  int32_t xcd_by_head;      // 1: the splits of one (group, row tile, head) share an XCD
   int32_t rope;             // 1: rotate the adapter key term
-  double rope_log2_theta;   // log2 of the rotary base
+  double rope_rev[kMaxRopePairs];  // theta^(-2i/d) / (2 pi): revolutions per position, pair i
 };
 
 struct BuildArgs {
@@ -101,7 +102,7 @@ struct PrefillArgs {
   float sm_scale;
   float sm_scale_log2;
   int32_t rope;
-  double rope_log2_theta;
+  double rope_rev[kMaxRopePairs];
 };
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, hipStream_t stream);

@@ -47,7 +47,6 @@ DecodePlan decode_plan(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
     p.split = max_ctx;
     p.nsplit = 1;
     p.part_stride = 0;
-    p.counter_bytes = 0;
     p.partial_bytes = 0;
     return p;
   }
@@ -64,9 +63,8 @@ DecodePlan decode_plan(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
   if (ceil_div(max_ctx, split) > kMaxSplits) split = (long long)round_up((size_t)ceil_div(max_ctx, kMaxSplits), granule);
   p.split = (int)split;
   p.nsplit = ceil_div(max_ctx, split);
-  p.part_stride = 4 + d + p.rp;
+  p.part_stride = 4 + d;  // [m, l, seq, nact, O'[d]] per row
   const size_t tiles = (size_t)num_groups * p.row_tiles * Hkv;
-  p.counter_bytes = round_up(tiles * sizeof(unsigned), 256);
   p.partial_bytes = p.nsplit > 1 ? tiles * p.nsplit * 16 * (size_t)p.part_stride * sizeof(float) : 0;
   return p;
 }
@@ -81,12 +79,19 @@ int check_decode_sizes(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
   if (dtype == LRA_F32 && d != 64 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "fp32 kernel supports d = 64 or 128 (got %d)", d);
   if (max_rank < 1 || max_rank > 64) return fail(LRA_ERR_UNSUPPORTED, "max_rank must be in 1..64 (got %d)", max_rank);
   if (max_ctx < 1) return fail(LRA_ERR_INVALID_ARG, "max_context_len must be >= 1 (got %d)", max_ctx);
+  if (dtype == LRA_BF16 && max_ctx > kMaxSplits * kMaxSplitBlocks * kBlock)
+    return fail(LRA_ERR_UNSUPPORTED, "bf16 decode supports contexts up to %d tokens (got %d)",
+                kMaxSplits * kMaxSplitBlocks * kBlock, max_ctx);
   if (S > 0 && (num_groups < 1 || num_groups > S))
     return fail(LRA_ERR_INVALID_ARG, "num_groups must be in 1..S (got %d, S=%d)", num_groups, S);
   return LRA_OK;
 }
 
-double log2_theta(float theta) { return theta > 0.f ? log2((double)theta) : 0.0; }
+// Revolutions per position of rotary pair i: theta^(-2i/d) / (2 pi), in fp64.
+void rope_table(double* out, float theta, int d) {
+  for (int i = 0; i < kMaxRopePairs; ++i)
+    out[i] = (theta > 0.f && i < d / 2) ? pow((double)theta, -2.0 * i / d) / (2.0 * M_PI) : 0.0;
+}
 
 }  // namespace
 }  // namespace lra
@@ -161,14 +166,7 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
 size_t lora_attn_decode_workspace_size(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
                                        int32_t max_rank, int32_t max_context_len, int32_t dtype) {
   if (S <= 0 || check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) != LRA_OK) return 0;
-  const DecodePlan p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
-  return p.counter_bytes + p.partial_bytes;
-}
-
-size_t lora_attn_decode_counter_bytes(int32_t S, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
-                                      int32_t max_rank, int32_t max_context_len, int32_t dtype) {
-  if (S <= 0 || check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) != LRA_OK) return 0;
-  return decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype).counter_bytes;
+  return decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype).partial_bytes;
 }
 
 int lora_attn_decode(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
@@ -194,7 +192,7 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
     return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
   const DecodePlan p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
-  const size_t need = p.counter_bytes + p.partial_bytes;
+  const size_t need = p.partial_bytes;
   if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed (got %zu)", need, workspace_bytes);
 
@@ -212,8 +210,7 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   a.bv = b_v;
   a.ranks = ranks;
   a.out = out;
-  a.counters = (unsigned*)workspace;
-  a.partials = need ? (float*)((char*)workspace + p.counter_bytes) : nullptr;
+  a.partials = need ? (float*)workspace : nullptr;
   a.max_blocks = max_blocks;
   a.num_groups = num_groups;
   a.S = S;
@@ -230,7 +227,14 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   a.sm_scale = sm_scale;
   a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.rope = rope_theta > 0.f;
-  a.rope_log2_theta = log2_theta(rope_theta);
+  rope_table(a.rope_rev, rope_theta, d);
+  {
+    // keep a head's splits on one XCD (its partials stay in that L2) unless
+    // the low-rank rows shared across heads outweigh the base rows
+    const long long lr_bytes_per_token = 4LL * (S - num_groups + 1 < p.apt ? S - num_groups + 1 : p.apt) *
+                                         p.row_tiles * p.rp;
+    a.xcd_by_head = 4 * lr_bytes_per_token <= 4LL * Hkv * d;
+  }
   const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, (hipStream_t)stream)
                                          : launch_decode_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
@@ -295,7 +299,7 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
   a.sm_scale = sm_scale;
   a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.rope = rope_theta > 0.f;
-  a.rope_log2_theta = log2_theta(rope_theta);
+  rope_table(a.rope_rev, rope_theta, d);
   const hipError_t e = launch_prefill_bf16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_prefill launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -121,3 +121,24 @@ def test_serving_mix_full_size_sampled():
     rng = np.random.default_rng(1)
     pick = sorted(set([int(lens.argmax()), int(lens.argmin())] + rng.choice(w.S, 6, replace=False).tolist()))
     _check(w, TOL_BF16, seqs=pick)
+
+
+def test_workspace_contents_do_not_matter():
+    """Split records are fully rewritten by each call: a workspace full of NaN
+    bytes, or one left over from a call with other shapes, gives the same bits
+    as a zeroed one. Groups of different lengths make some rows finish in the
+    main kernel while others are combined."""
+    from tests.gpu_harness import decode_workspace
+
+    w = decode_workload(name="ws", group_sizes=(2, 1, 3), context_lens=(700, 16, 2500), ranks=(16,) * 6,
+                        shared_l=True, seed=12)
+    dw = upload(w)
+    ws = decode_workspace(dw)
+    ref = to_np(run_decode(dw, workspace=ws))
+    ws.fill_(0xFF)  # every float is NaN
+    assert np.array_equal(to_np(run_decode(dw, workspace=ws)), ref)
+    other = upload(decode_workload(name="ws2", group_sizes=(4,), context_lens=(5000,), ranks=(16,) * 4, seed=13))
+    n = max(decode_workspace(other).numel(), ws.numel())
+    big = torch.zeros(n, dtype=torch.uint8, device="cuda")
+    run_decode(other, workspace=big)
+    assert np.array_equal(to_np(run_decode(dw, workspace=big)), ref)
