@@ -46,6 +46,8 @@ def _args():
     ap.add_argument("--legs", default="decode,prefill,long,mix,tiny")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
     return ap.parse_args()
 
 
@@ -352,6 +354,17 @@ def main():
     import torch
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib:
+        # a plain copy of known size: HBM counters per dispatch should read
+        # this many bytes fetched and written
+        n = args.calibrate_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": n, "launches": 5}))
+        return
     legs = set(args.legs.split(","))
     K, W = args.steps, args.warmup
 
