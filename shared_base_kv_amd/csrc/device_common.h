@@ -78,17 +78,21 @@ __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48) that
+// hold the same accumulator column, with the gfx950 row-swap moves (plain
+// VALU data movement, no LDS round trip). Each step combines a lane's value
+// with the partner row's, in an order that is the same for both partners.
 __device__ __forceinline__ float wave_max_across_groups(float v) {
-  // Reduce over the 4 lane groups (lanes l, l^16, l^32, l^48) that hold the
-  // same accumulator column.
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_across_groups(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

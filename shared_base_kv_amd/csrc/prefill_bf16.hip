@@ -24,6 +24,18 @@
 //   O^T[dim, row]  += V^T P^T            (16x16x32, V^T from LDS, P^T from the S^T accumulators)
 //   C^T[rank, row] += L_v^T P^T
 //   O^T            += B_v^T C^T          (after the loop; C split into bf16 hi + lo)
+//
+// Software pipeline (one barrier per tile): while the matrix cores work on
+// the scores of tile t and on P V of tile t-1, the vector units rebuild the
+// keys of tile t+1 into the other key buffer and the loads of tile t+2 are
+// in flight; then the softmax of tile t runs. Keys are double-buffered in
+// LDS, V^T and L_v^T triple-buffered (tile t-1 is still read while t+1 is
+// written). The rotation of the adapter key at position 64t + o is split by
+// angle addition into a per-tile part (64t, one table of 64 pairs per tile)
+// and a per-lane part (o, fixed for the whole loop), so no transcendental is
+// evaluated per element.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -35,18 +47,35 @@ constexpr int kRows = 128;     // query rows per workgroup
 constexpr int kTile = 64;      // keys per tile (4 cache blocks)
 constexpr int kKPitch = D + 8;          // LDS row pitch of the key tile (bf16)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
+constexpr int kKBufs = 2;
+constexpr int kVBufs = 3;
+
+// (cos, sin) of one angle given in revolutions, with the revolution count
+// reduced exactly in fp64 first.
+__device__ __forceinline__ float2 cos_sin_rev(double x) {
+  const float f = (float)(x - __builtin_floor(x));
+  return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
+
+template <int RP>
+struct TileRegs {  // this wave's cache block of one tile, on its way from HBM
+  uint2 kbl[4], kbh[4];  // base keys, dims 16cb + 4lg .. +3 and +64, of key lc
+  uint4 vv[4];           // V^T rows 2 lane + u/2, keys 8 (u%2) .. +7 of the block
+  uint4 lk[RP == 64 ? 2 : 1];  // L_k row of key lc: ranks 8lg.. (RP 32/64) or 4lg.. (RP 16, .x .y)
+  uint4 lvv[2];          // L_v^T items lane, lane + 64: rank item/2, keys 8 (item%2) .. +7
+};
 
 template <int RP>
 __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NRT = RP / 16;
   constexpr int KC = RP >= 32 ? RP / 32 : 1;
-  __shared__ __align__(16) uint16_t s_k[kTile * kKPitch];   // rebuilt keys [key][dim]
-  __shared__ __align__(16) uint16_t s_v[D * kVPitch];       // V^T [dim][key]
-  __shared__ __align__(16) uint16_t s_lv[RP * kVPitch];     // L_v^T [rank][key]
-  __shared__ __align__(16) uint16_t s_bt[D * RP];           // B_k^T [dim][rank]
-  __shared__ __align__(16) uint16_t s_bvt[D * RP];          // B_v^T [dim][rank]
+  __shared__ __align__(16) uint16_t s_k[kKBufs][kTile * kKPitch];   // rebuilt keys [key][dim]
+  __shared__ __align__(16) uint16_t s_v[kVBufs][D * kVPitch];       // V^T [dim][key]
+  __shared__ __align__(16) uint16_t s_lv[kVBufs][RP * kVPitch];     // L_v^T [rank][key]
+  __shared__ __align__(16) uint16_t s_bt[D * RP];                   // B_k^T [dim][rank]
+  __shared__ __align__(16) uint16_t s_bvt[D * RP];                  // B_v^T [dim][rank]
+  __shared__ __align__(16) float s_rot[kKBufs][2 * kMaxRopePairs];  // (cos, sin) of 64 t theta_i
   __shared__ double s_rev[kMaxRopePairs];
-  __shared__ int s_phys[kTile / kBlock];
 
   const int G = a.G;
   const int TQ = kRows / G;  // query tokens per workgroup
@@ -81,23 +110,47 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
   const int lc = lane & 15;
   const int lg = lane >> 4;
 
-  // ---- preamble: B_k^T, B_v^T, rotary table ----
+  // ---- preamble: B_k^T, B_v^T, rotary tables ----
   for (int e = tid; e < RP * (D / 8); e += 256) {
     const int k = e % RP, d8 = (e / RP) * 8;
-    uint4 vk = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    uint4 vk = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
     if (k < r) {
       vk = ld16(bk + (size_t)k * HD + h * D + d8);
-      vv = ld16(bv + (size_t)k * HD + h * D + d8);
+      vw = ld16(bv + (size_t)k * HD + h * D + d8);
     }
     const uint16_t* pk = reinterpret_cast<const uint16_t*>(&vk);
-    const uint16_t* pv = reinterpret_cast<const uint16_t*>(&vv);
+    const uint16_t* pv = reinterpret_cast<const uint16_t*>(&vw);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       s_bt[(d8 + i) * RP + k] = pk[i];
       s_bvt[(d8 + i) * RP + k] = pv[i];
     }
   }
+  // rotary revolutions per position, staged through LDS (a lane-indexed read
+  // of the kernel-argument array would go through scratch)
   if (tid < kMaxRopePairs) s_rev[tid] = a.rope_rev[tid];
+  __syncthreads();
+  // per-tile table: every wave computes pair `lane` and writes the same value
+  const double rev_lane = s_rev[lane];
+  auto rot_table = [&](int t) __attribute__((always_inline)) {
+    const float2 cs = cos_sin_rev((double)(t * kTile) * rev_lane);
+    *reinterpret_cast<float2*>(&s_rot[t & 1][2 * lane]) = cs;
+  };
+  rot_table(0);
+  rot_table(1);
+  // per-lane part: key offset 16 wave + lc within the tile, pairs 16cb + 4lg + jj
+  float co[4][4], so[4][4];
+  {
+    const double off = (double)(kBlock * wave + lc);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float2 cs = cos_sin_rev(off * s_rev[16 * cb + 4 * lg + jj]);
+        co[cb][jj] = cs.x;
+        so[cb][jj] = cs.y;
+      }
+  }
 
   // ---- query operands: this wave's rows 32w + 16rt + lc ----
   bf16x8 qb[2][4];
@@ -127,131 +180,137 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
 #pragma unroll
     for (int i = 0; i < NRT; ++i) cacc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const bf16x8 zero8 = as_bf16x8(make_uint4(0, 0, 0, 0));
   const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
   const int n_tiles = (kv_end + kTile - 1) / kTile;
+  const float csc = a.sm_scale_log2;
 
-  for (int kt = 0; kt < n_tiles; ++kt) {
-    const int kbase = kt * kTile;
-    __syncthreads();  // previous tile's LDS reads are done
-    if (tid < kTile / kBlock) s_phys[tid] = (kbase + kBlock * tid < kv_end) ? bt_row[kbase / kBlock + tid] : -1;
-    __syncthreads();
-
-    // ---- wave w: block w of the tile -> rebuilt keys, V^T and L_v^T into LDS ----
-    {
-      const int b = wave;
-      const int phys = uniform(s_phys[b]);
-      const int key0 = kbase + kBlock * b;
-      if (phys >= 0) {
-        const uint16_t* kp = (const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D;
-        const uint16_t* vp = (const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock;
-        // V^T: 128 dims x 16 keys of this block; keys past the sequence read as zero
-        const auto rv = buf_rsrc(vp, D * kBlock * 2);
+  // ---- global -> registers: block `wave` of tile t. Blocks past the
+  // visible keys get zero-length buffer ranges, so their loads return 0. ----
+  TileRegs<RP> tr;
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * kTile + kBlock * wave;
+    const bool valid = key0 < kv_end;
+    const int phys = uniform(bt_row[valid ? key0 / kBlock : 0]);
+    const int on = valid ? 1 : 0;
+    const auto rk = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
+                             on * kBlock * D * 2);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int dim = 2 * lane + (u >> 1), half = u & 1;  // lane covers dims 2lane, 2lane+1
-          uint4 v = bld16(rv, (dim * kBlock + 8 * half) * 2);
-          const int kk = key0 + 8 * half;
+    for (int cb = 0; cb < 4; ++cb) {
+      tr.kbl[cb] = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
+      tr.kbh[cb] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
+    }
+    const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, on * kBlock * r * 2);
+    if constexpr (RP == 16) {
+      const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
+      tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        tr.lk[kc] = bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
+    }
+    const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
+                             on * D * kBlock * 2);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) tr.vv[u] = bld16(rv, ((2 * lane + (u >> 1)) * kBlock + 8 * (u & 1)) * 2);
+    const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, on * r * kBlock * 2);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = lane + 64 * u, rank = e >> 1;
+      tr.lvv[u] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
+    }
+  };
+
+  // ---- registers -> LDS: V^T, L_v^T as loaded; keys rebuilt as
+  // K_base + rope(B_k^T L_k^T), rounded once to bf16. LAST marks the final
+  // tile, the only one that can hold positions >= T (zeroed in V and L_v,
+  // whose products with P = 0 must stay finite). ----
+  auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int key0 = t * kTile + kBlock * wave;
+    uint16_t* sk = s_k[t & 1];
+    uint16_t* sv = s_v[t % kVBufs];
+    uint16_t* slv = s_lv[t % kVBufs];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint4 v = tr.vv[u];
+      if constexpr (LAST) {
+        const int kk = key0 + 8 * (u & 1);
+        uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+          w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
+      }
+      *reinterpret_cast<uint4*>(sv + (2 * lane + (u >> 1)) * kVPitch + kBlock * wave + 8 * (u & 1)) = v;
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int e = lane + 64 * u;
+      if (e < 2 * RP) {
+        uint4 v = tr.lvv[u];
+        if constexpr (LAST) {
+          const int kk = key0 + 8 * (e & 1);
           uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t m = (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
-            w32[p] &= m;
-          }
-          *reinterpret_cast<uint4*>(s_v + dim * kVPitch + kBlock * b + 8 * half) = v;
+          for (int p = 0; p < 4; ++p)
+            w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
         }
-        // L_v^T: ranks x 16 keys
-        const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, r * kBlock * 2);
-        for (int e = lane; e < RP * 2; e += 64) {
-          const int rank = e >> 1, half = e & 1;
-          uint4 v = bld16(rlv, rank < r ? (rank * kBlock + 8 * half) * 2 : kOob);
-          const int kk = key0 + 8 * half;
-          uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const uint32_t m = (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
-            w32[p] &= m;
-          }
-          *reinterpret_cast<uint4*>(s_lv + rank * kVPitch + kBlock * b + 8 * half) = v;
-        }
-        // rebuilt keys: X^T = B_k^T L_k^T for this block, rotated, plus the base key
-        const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, kBlock * r * 2);
-        uint2 lk16 = make_uint2(0, 0);
-        bf16x8 lk32[KC];
-        if constexpr (RP == 16) {
-          lk16 = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
-        } else {
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            lk32[kc] = as_bf16x8(bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob));
-        }
-        const auto rk = buf_rsrc(kp, kBlock * D * 2);
-        const double pd = (double)(key0 + lc);
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
-          if constexpr (RP == 16) {
-            const uint2 al_ = *reinterpret_cast<const uint2*>(s_bt + (16 * cb + lc) * RP + 4 * lg);
-            const uint2 ah_ = *reinterpret_cast<const uint2*>(s_bt + (16 * (cb + 4) + lc) * RP + 4 * lg);
-            xl = mfma16(as_i16x4(al_), as_i16x4(lk16), xl);
-            xh = mfma16(as_i16x4(ah_), as_i16x4(lk16), xh);
-          } else {
-#pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-              const uint4 al_ = *reinterpret_cast<const uint4*>(s_bt + (16 * cb + lc) * RP + 32 * kc + 8 * lg);
-              const uint4 ah_ = *reinterpret_cast<const uint4*>(s_bt + (16 * (cb + 4) + lc) * RP + 32 * kc + 8 * lg);
-              xl = mfma32(as_bf16x8(al_), lk32[kc], xl);
-              xh = mfma32(as_bf16x8(ah_), lk32[kc], xh);
-            }
-          }
-          // lane: key lc of the block, dims 16cb + 4lg + jj and 64 + 16cb + 4lg + jj
-          const uint2 kl = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
-          const uint2 kh = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
-          const uint16_t* pkl = reinterpret_cast<const uint16_t*>(&kl);
-          const uint16_t* pkh = reinterpret_cast<const uint16_t*>(&kh);
-          float y1[4], y2[4];
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            float u = xl[jj], w = xh[jj];
-            if (a.rope) {
-              const double x = pd * s_rev[16 * cb + 4 * lg + jj];
-              const float f = (float)(x - __builtin_floor(x));
-              const float c = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
-              const float u2 = u * c - w * sn;
-              w = w * c + u * sn;
-              u = u2;
-            }
-            y1[jj] = bf16_to_f32(pkl[jj]) + u;
-            y2[jj] = bf16_to_f32(pkh[jj]) + w;
-          }
-          *reinterpret_cast<uint2*>(s_k + (kBlock * b + lc) * kKPitch + 16 * cb + 4 * lg) =
-              pack_bf16x4(y1[0], y1[1], y1[2], y1[3]);
-          *reinterpret_cast<uint2*>(s_k + (kBlock * b + lc) * kKPitch + 64 + 16 * cb + 4 * lg) =
-              pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
-        }
-      } else {
-        // block past the visible keys: zero keys, values and low-rank rows
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int dim = 2 * lane + (u >> 1), half = u & 1;
-          *reinterpret_cast<uint4*>(s_v + dim * kVPitch + kBlock * b + 8 * half) = make_uint4(0, 0, 0, 0);
-        }
-        for (int e = lane; e < RP * 2; e += 64)
-          *reinterpret_cast<uint4*>(s_lv + (e >> 1) * kVPitch + kBlock * b + 8 * (e & 1)) = make_uint4(0, 0, 0, 0);
-        for (int e = lane; e < kBlock * (D / 8); e += 64)
-          *reinterpret_cast<uint4*>(s_k + (kBlock * b + e / (D / 8)) * kKPitch + 8 * (e % (D / 8))) = make_uint4(0, 0, 0, 0);
+        *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * wave + 8 * (e & 1)) = v;
       }
     }
-    __syncthreads();
+    const float* rot = s_rot[t & 1];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+      f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (RP == 16) {
+        const uint2 al_ = *reinterpret_cast<const uint2*>(s_bt + (16 * cb + lc) * RP + 4 * lg);
+        const uint2 ah_ = *reinterpret_cast<const uint2*>(s_bt + (16 * (cb + 4) + lc) * RP + 4 * lg);
+        const uint2 lk2 = make_uint2(tr.lk[0].x, tr.lk[0].y);
+        xl = mfma16(as_i16x4(al_), as_i16x4(lk2), xl);
+        xh = mfma16(as_i16x4(ah_), as_i16x4(lk2), xh);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 al_ = *reinterpret_cast<const uint4*>(s_bt + (16 * cb + lc) * RP + 32 * kc + 8 * lg);
+          const uint4 ah_ = *reinterpret_cast<const uint4*>(s_bt + (16 * (cb + 4) + lc) * RP + 32 * kc + 8 * lg);
+          xl = mfma32(as_bf16x8(al_), as_bf16x8(tr.lk[kc]), xl);
+          xh = mfma32(as_bf16x8(ah_), as_bf16x8(tr.lk[kc]), xh);
+        }
+      }
+      const float4 r01 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg));
+      const float4 r23 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg) + 4);
+      const float cB[4] = {r01.x, r01.z, r23.x, r23.z};
+      const float sB[4] = {r01.y, r01.w, r23.y, r23.w};
+      const float kl[4] = {__uint_as_float(tr.kbl[cb].x << 16), __uint_as_float(tr.kbl[cb].x & 0xFFFF0000u),
+                           __uint_as_float(tr.kbl[cb].y << 16), __uint_as_float(tr.kbl[cb].y & 0xFFFF0000u)};
+      const float kh[4] = {__uint_as_float(tr.kbh[cb].x << 16), __uint_as_float(tr.kbh[cb].x & 0xFFFF0000u),
+                           __uint_as_float(tr.kbh[cb].y << 16), __uint_as_float(tr.kbh[cb].y & 0xFFFF0000u)};
+      float y1[4], y2[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // angle of pair 16cb + 4lg + jj at position 64t + 16 wave + lc
+        const float c = cB[jj] * co[cb][jj] - sB[jj] * so[cb][jj];
+        const float sn = sB[jj] * co[cb][jj] + cB[jj] * so[cb][jj];
+        const float u = xl[jj], w = xh[jj];
+        y1[jj] = __builtin_fmaf(-w, sn, __builtin_fmaf(u, c, kl[jj]));
+        y2[jj] = __builtin_fmaf(u, sn, __builtin_fmaf(w, c, kh[jj]));
+      }
+      *reinterpret_cast<uint2*>(sk + (kBlock * wave + lc) * kKPitch + 16 * cb + 4 * lg) =
+          pack_bf16x4(y1[0], y1[1], y1[2], y1[3]);
+      *reinterpret_cast<uint2*>(sk + (kBlock * wave + lc) * kKPitch + 64 + 16 * cb + 4 * lg) =
+          pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
+    }
+  };
 
-    // ---- scores S^T[key, row] for the 4 key blocks x this wave's 2 row tiles ----
-    f32x4 sacc[4][2];
+  // ---- S^T[key, row] for the tile's 4 key blocks x this wave's 2 row tiles ----
+  f32x4 sacc[4][2];
+  auto scores = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* sk = s_k[t & 1];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       bf16x8 kop[4];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks)
-        kop[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(s_k + (kBlock * kb + lc) * kKPitch + 32 * ks + 8 * lg));
+        kop[ks] = as_bf16x8(*reinterpret_cast<const uint4*>(sk + (kBlock * kb + lc) * kKPitch + 32 * ks + 8 * lg));
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         sacc[kb][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -259,51 +318,18 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
         for (int ks = 0; ks < 4; ++ks) sacc[kb][rt] = mfma32(kop[ks], qb[rt][ks], sacc[kb][rt]);
       }
     }
-    // ---- causal online softmax (base 2) per row ----
-    bf16x8 pop[2][2];  // P^T operands: [row tile][key pair (blocks 2kp, 2kp+1)]
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
-      float sv[4][4];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int key = kbase + kBlock * kb + 4 * lg + jj;
-          const bool vis = key <= rpos[rt] && key < kv_end;
-          sv[kb][jj] = vis ? sacc[kb][rt][jj] * a.sm_scale_log2 : -INFINITY;
-          mx = fmaxf(mx, sv[kb][jj]);
-        }
-      mx = wave_max_across_groups(mx);
-      const float m_new = fmaxf(m_run[rt], mx);
-      // a row that sees no key of this tile keeps its state (m_new may be -inf)
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run[rt] - m_new);
-      float psum = 0.f;
-      float pv[4][4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          pv[kb][jj] = (m_new == -INFINITY) ? 0.f : fast_exp2(sv[kb][jj] - m_new);
-          psum += pv[kb][jj];
-        }
-      l_run[rt] = l_run[rt] * alpha + psum;
-      m_run[rt] = m_new;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) o[rt][i] *= alpha;
-#pragma unroll
-      for (int i = 0; i < NRT; ++i) cacc[rt][i] *= alpha;
-#pragma unroll
-      for (int kp = 0; kp < 2; ++kp)
-        pop[rt][kp] = cat8(pack_bf16x4(pv[2 * kp][0], pv[2 * kp][1], pv[2 * kp][2], pv[2 * kp][3]),
-                           pack_bf16x4(pv[2 * kp + 1][0], pv[2 * kp + 1][1], pv[2 * kp + 1][2], pv[2 * kp + 1][3]));
-    }
-    // ---- O^T += V^T P^T ; C^T += L_v^T P^T ----
+  };
+
+  // ---- O^T += V^T P^T ; C^T += L_v^T P^T for tile t with the P^T operands ----
+  bf16x8 pop[2][2];  // [row tile][key pair (blocks 2kp, 2kp+1)]
+  auto pv = [&](int t) __attribute__((always_inline)) {
+    const uint16_t* sv = s_v[t % kVBufs];
+    const uint16_t* slv = s_lv[t % kVBufs];
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        const uint16_t* vr = s_v + (16 * db + lc) * kVPitch + 32 * kp + 4 * lg;
+        const uint16_t* vr = sv + (16 * db + lc) * kVPitch + 32 * kp + 4 * lg;
         const bf16x8 vop = cat8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + kBlock));
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) o[rt][db] = mfma32(vop, pop[rt][kp], o[rt][db]);
@@ -313,13 +339,112 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
     for (int rr = 0; rr < NRT; ++rr) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        const uint16_t* lr = s_lv + (16 * rr + lc) * kVPitch + 32 * kp + 4 * lg;
+        const uint16_t* lr = slv + (16 * rr + lc) * kVPitch + 32 * kp + 4 * lg;
         const bf16x8 lop = cat8(*reinterpret_cast<const uint2*>(lr), *reinterpret_cast<const uint2*>(lr + kBlock));
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) cacc[rt][rr] = mfma32(lop, pop[rt][kp], cacc[rt][rr]);
       }
     }
+  };
+
+  // ---- online softmax (base 2) of tile t; MASK applies causality and the
+  // visible-key bound, needed only on tiles that reach past the first row ----
+  auto softmax = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int kbase = t * kTile;
+    float alpha[2];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          if constexpr (MASK) {
+            const int key = kbase + kBlock * kb + 4 * lg + jj;
+            const bool vis = key <= rpos[rt] && key < kv_end;
+            sacc[kb][rt][jj] = vis ? sacc[kb][rt][jj] : -INFINITY;
+          }
+          mx = fmaxf(mx, sacc[kb][rt][jj]);
+        }
+      mx = wave_max_across_groups(mx);
+      const float m_new = fmaxf(m_run[rt], mx * csc);
+      // with MASK a row may have seen no key yet (m_new = -inf): keep its state
+      const bool dead = MASK && m_new == -INFINITY;
+      alpha[rt] = dead ? 1.f : fast_exp2(m_run[rt] - m_new);
+      const float nm = dead ? 0.f : -m_new;
+      float psum = 0.f;
+      float pv_[4][4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          pv_[kb][jj] = fast_exp2(__builtin_fmaf(sacc[kb][rt][jj], csc, nm));
+          psum += pv_[kb][jj];
+        }
+      l_run[rt] = l_run[rt] * alpha[rt] + psum;
+      m_run[rt] = m_new;
+#pragma unroll
+      for (int kp = 0; kp < 2; ++kp)
+        pop[rt][kp] = cat8(pack_bf16x4(pv_[2 * kp][0], pv_[2 * kp][1], pv_[2 * kp][2], pv_[2 * kp][3]),
+                           pack_bf16x4(pv_[2 * kp + 1][0], pv_[2 * kp + 1][1], pv_[2 * kp + 1][2], pv_[2 * kp + 1][3]));
+    }
+    // rescale the accumulators only when some row's running max moved
+    if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[rt][i] *= alpha[rt];
+#pragma unroll
+        for (int i = 0; i < NRT; ++i) cacc[rt][i] *= alpha[rt];
+      }
+    }
+  };
+  auto softmax_tile = [&](int t) __attribute__((always_inline)) {
+    if (t * kTile + kTile - 1 > p0)
+      softmax(t, std::true_type{});
+    else
+      softmax(t, std::false_type{});
+  };
+
+  // ---- pipeline ----
+  __syncthreads();  // B_k^T, B_v^T and the first rotary tables are in LDS
+  load_tile(0);
+  if (n_tiles == 1)
+    store_tile(0, std::true_type{});
+  else
+    store_tile(0, std::false_type{});
+  if (n_tiles > 1) load_tile(1);
+  __syncthreads();
+  // tile 0
+  scores(0);
+  if (n_tiles > 2) {
+    store_tile(1, std::false_type{});
+    load_tile(2);
+    rot_table(2);
+  } else if (n_tiles == 2) {
+    store_tile(1, std::true_type{});
   }
+  softmax_tile(0);
+  __syncthreads();
+  int kt = 1;
+  for (; kt + 2 < n_tiles; ++kt) {  // steady state
+    scores(kt);
+    pv(kt - 1);
+    store_tile(kt + 1, std::false_type{});
+    load_tile(kt + 2);
+    rot_table(kt + 2);
+    softmax_tile(kt);
+    __syncthreads();
+  }
+  for (; kt < n_tiles; ++kt) {  // the last one or two tiles
+    scores(kt);
+    pv(kt - 1);
+    if (kt + 1 < n_tiles) store_tile(kt + 1, std::true_type{});
+    softmax_tile(kt);
+    __syncthreads();
+  }
+  pv(n_tiles - 1);
 
   // ---- epilogue: O^T += B_v^T C^T (C as bf16 hi + lo), divide by l, store ----
 #pragma unroll
