@@ -12,23 +12,31 @@
 //
 // Work decomposition. One workgroup = (group g, row tile rt, split c, KV
 // head h). A group is a set of sequences sharing one base context; a row
-// tile holds up to 16 query rows (apt sequences x G query heads of head h),
-// so the base K/V of a block is read once for all agents of the tile. A
-// split is a contiguous token range; its 4 waves take interleaved 32-token
-// steps and keep independent online-softmax states, merged in LDS at the
-// end. Each wave loads step i+1 while it computes step i. Splits of one
-// (g, rt, h) meet in the last-arriving workgroup, which merges their partial
-// states and finishes the rows (adds (P L_v) B_v, divides by the softmax
-// sum, rounds to bf16).
+// tile holds up to 16 query rows (up to NA sequences x G query heads of head
+// h), so the base K/V of a block is read once for all agents of the tile. A
+// split is a contiguous token range; its 8 waves take interleaved 16-token
+// cache blocks, two blocks in flight per wave, and keep independent
+// online-softmax states, merged in LDS at the end. The merged state of the
+// split gets its value adapter term on MFMA and is written as one record per
+// row; a second kernel merges the records of all splits.
 //
 // Matrix-core mapping (16x16 MFMA tiles, tokens on the M side):
 //   S^T[token, row]   = K_base[token, :] Q^T            (16x16x32)
 //                     + sum_a Y_a[token, :] Qmask_a^T    (16x16x32, Y_a = rotated rebuild)
 //   X_a^T[dim, token] = B_k,a^T[dim, :] L_k^T[:, token]  (16x16x16 or 16x16x32 over rank)
-//   O^T[dim, row]    += V^T[dim, token] P^T[token, row]  (16x16x32 over two blocks)
+//   O^T[dim, row]    += V^T[dim, token] P^T[token, row]  (16x16x16 over the block)
 //   C^T[rank, row]   += L_v^T[rank, token] P^T[token, row]
+//   O'^T[dim, row]    = O^T + B_v,a^T[dim, rank] C^T[rank, row]  (after the merge; C as bf16 hi + lo)
 // The accumulator layout of one product is the operand layout of the next,
 // so rebuilt keys and probabilities never leave registers.
+//
+// Rotation angles: the angle of pair i at position tb + lc (block start tb,
+// lane column lc) is split by angle addition into a per-block part (64
+// pairs, computed by the wave once per block, one pair per lane) and a
+// per-column part (a table of 16 x 64 pairs built once per workgroup), so
+// no transcendental is evaluated per element.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,7 +44,8 @@ namespace lra {
 namespace {
 
 constexpr int D = 128;
-constexpr int kLdsMain = 65536;
+constexpr int kQPitch = D + 8;                    // LDS row pitch of the query tile (bf16)
+constexpr int kRotPitch = 2 * kMaxRopePairs + 4;  // LDS row pitch of the per-column rotation table (floats)
 
 struct TileAgent {
   const uint16_t* lk;
@@ -47,277 +56,31 @@ struct TileAgent {
   int seq;
 };
 
-// Registers of one 32-token step of one wave: base K rows, V^T rows and the
-// low-rank rows of the tile's first agent (every agent's, when shared).
+__device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<const uint16_t*>(((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ float2 cos_sin_rev(double x) {
+  const float f = (float)(x - __builtin_floor(x));
+  return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
+}
+
+// Registers of one 16-token cache block of one wave: base K rows, V^T rows
+// and the low-rank rows of the tile's first agent (every agent's, when the
+// agents share their low-rank pools).
 template <int RP>
-struct Step {
+struct Blk {
   static constexpr int KC = RP >= 32 ? RP / 32 : 1;
-  static constexpr bool kLv = RP <= 32;  // at rank 64 L_v rows are read at use (register budget)
-  bf16x8 kr[2][4];
-  uint2 vr[2][8];
-  uint2 lk16[2];
-  bf16x8 lk32[2][KC];
-  uint2 lv[2][kLv ? RP / 16 : 1];
-  int tb;
-  int nblk;
-  int phys[2];
+  static constexpr int NRT = RP / 16;
+  bf16x8 kr[4];     // K_base[token lc][dims 32ks + 8lg .. +7]
+  uint2 vr[8];      // V^T[dim 16cb + lc][tokens 4lg .. +3]
+  uint2 lk16;       // L_k[token lc][ranks 4lg .. +3]              (RP 16)
+  bf16x8 lk32[KC];  // L_k[token lc][ranks 32kc + 8lg .. +7]       (RP 32, 64)
+  uint2 lv[NRT];    // L_v[rank 16rr + lc][tokens 4lg .. +3]
 };
-
-// Loads of one step. Each (block, head) chunk of the pools gets its own
-// buffer resource; lanes whose rank slot is past the agent's rank read zero.
-template <int RP>
-__device__ __forceinline__ void load_step_k(Step<RP>& s, const DecodeArgs& a, int tb, int t_end, int p0, int p1,
-                                            int h, int lc, int lg) {
-  s.tb = tb;
-  s.nblk = (t_end - tb) > kBlock ? 2 : 1;
-  s.phys[0] = uniform(p0);
-  s.phys[1] = uniform(s.nblk > 1 ? p1 : p0);
-  const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b < s.nblk) {
-      const auto r = buf_rsrc((const uint16_t*)a.kb + (size_t)s.phys[b] * blk_elems + (size_t)h * kBlock * D,
-                              kBlock * D * 2);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.kr[b][ks] = as_bf16x8(bld16(r, (lc * D + 8 * lg + 32 * ks) * 2));
-    } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) s.kr[b][ks] = as_bf16x8(make_uint4(0, 0, 0, 0));
-    }
-  }
-}
-
-// Values are issued after keys and low-rank rows: loads complete in issue
-// order, so the scores of a step can start before its values arrive.
-template <int RP>
-__device__ __forceinline__ void load_step_v(Step<RP>& s, const DecodeArgs& a, int h, int lc, int lg) {
-  const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b < s.nblk) {
-      const auto r = buf_rsrc((const uint16_t*)a.vb + (size_t)s.phys[b] * blk_elems + (size_t)h * D * kBlock,
-                              kBlock * D * 2);
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) s.vr[b][cb] = bld8(r, ((16 * cb + lc) * kBlock + 4 * lg) * 2);
-    } else {
-#pragma unroll
-      for (int cb = 0; cb < 8; ++cb) s.vr[b][cb] = make_uint2(0, 0);
-    }
-  }
-}
-
-// Low-rank key operand of block b for one agent: L_k[token lc][rank slots].
-template <int RP>
-__device__ __forceinline__ void load_lk(const TileAgent& ag, int phys, int lc, int lg, uint2& lk16,
-                                        bf16x8 (&lk32)[RP >= 32 ? RP / 32 : 1]) {
-  const auto r = buf_rsrc(ag.lk + (size_t)phys * kBlock * ag.r, kBlock * ag.r * 2);
-  if constexpr (RP == 16) {
-    lk16 = bld8(r, (4 * lg < ag.r) ? (lc * ag.r + 4 * lg) * 2 : kOob);
-  } else {
-#pragma unroll
-    for (int kc = 0; kc < RP / 32; ++kc)
-      lk32[kc] = as_bf16x8(bld16(r, (32 * kc + 8 * lg < ag.r) ? (lc * ag.r + 32 * kc + 8 * lg) * 2 : kOob));
-  }
-}
-
-// Low-rank value operand of block b, rank tile rr: L_v[rank 16rr + lc][tokens 4lg..].
-__device__ __forceinline__ uint2 load_lv(const TileAgent& ag, int phys, int rr, int lc, int lg) {
-  const auto r = buf_rsrc(ag.lv + (size_t)phys * ag.r * kBlock, ag.r * kBlock * 2);
-  const int rank = 16 * rr + lc;
-  return bld8(r, rank < ag.r ? (rank * kBlock + 4 * lg) * 2 : kOob);
-}
-
-template <int RP>
-__device__ __forceinline__ void load_step_l(Step<RP>& s, const TileAgent& ag0, int lc, int lg) {
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    if (b < s.nblk) {
-      load_lk<RP>(ag0, s.phys[b], lc, lg, s.lk16[b], s.lk32[b]);
-      if constexpr (Step<RP>::kLv) {
-#pragma unroll
-        for (int rr = 0; rr < RP / 16; ++rr) s.lv[b][rr] = load_lv(ag0, s.phys[b], rr, lc, lg);
-      }
-    } else {
-      s.lk16[b] = make_uint2(0, 0);
-#pragma unroll
-      for (int kc = 0; kc < Step<RP>::KC; ++kc) s.lk32[b][kc] = as_bf16x8(make_uint4(0, 0, 0, 0));
-      if constexpr (Step<RP>::kLv) {
-#pragma unroll
-        for (int rr = 0; rr < RP / 16; ++rr) s.lv[b][rr] = make_uint2(0, 0);
-      }
-    }
-  }
-}
-
-constexpr int kQPitch = D + 8;  // LDS row pitch of the query tile (bf16), breaks bank aliasing
-
-struct Frame {  // per-lane constants of the main loop
-  const uint16_t* q;    // LDS query tile [16][kQPitch], this lane's row
-  const double* rev;    // LDS table: rotary revolutions per position of pair i
-  int row_al;           // sequence (agent slot) of this lane's query row
-  bool row_ok;
-};
-
-// S^T of one 16-token block: base part plus every agent's rebuilt adapter
-// part. The loop runs over rotation pairs (dim blocks cb, cb + 4) outside and
-// agents inside, so only one pair's cos/sin is live at a time.
-template <int RP>
-__device__ __forceinline__ f32x4 block_scores(const Step<RP>& s, const int b, const DecodeArgs& a, const Frame& fr,
-                                              const TileAgent* s_agent, const uint16_t* s_bt, int ns, bool shared_l,
-                                              int lc, int lg) {
-  const bf16x8 zero8 = as_bf16x8(make_uint4(0, 0, 0, 0));
-  f32x4 sacc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int ks = 0; ks < 4; ++ks) {
-    const bf16x8 qb = as_bf16x8(*reinterpret_cast<const uint4*>(fr.q + 32 * ks + 8 * lg));
-    sacc = mfma32(s.kr[b][ks], qb, sacc);
-  }
-  const double pd = (double)(s.tb + 16 * b + lc);
-#pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    float cs[4], sn[4];
-    if (a.rope) {
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const double x = pd * fr.rev[16 * cb + 4 * lg + jj];
-        const float f = (float)(x - __builtin_floor(x));
-        cs[jj] = __builtin_amdgcn_cosf(f);
-        sn[jj] = __builtin_amdgcn_sinf(f);
-      }
-    }
-    const bf16x8 qa = cat8(*reinterpret_cast<const uint2*>(fr.q + 16 * cb + 4 * lg),
-                           *reinterpret_cast<const uint2*>(fr.q + 64 + 16 * cb + 4 * lg));
-    for (int al = 0; al < ns; ++al) {
-      const TileAgent& ag = s_agent[al];
-      f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
-      const uint16_t* btp = s_bt + ((size_t)al * D + lc) * RP;
-      const bool own = al == 0 || shared_l;  // low-rank rows already in registers
-      uint2 lko16 = s.lk16[b];
-      bf16x8 lko32[Step<RP>::KC];
-#pragma unroll
-      for (int kc = 0; kc < Step<RP>::KC; ++kc) lko32[kc] = s.lk32[b][kc];
-      if (!own) load_lk<RP>(ag, s.phys[b], lc, lg, lko16, lko32);
-      if constexpr (RP == 16) {
-        const uint2 lk = lko16;
-        const uint2 al_ = *reinterpret_cast<const uint2*>(btp + (size_t)16 * cb * RP + 4 * lg);
-        const uint2 ah_ = *reinterpret_cast<const uint2*>(btp + (size_t)16 * (cb + 4) * RP + 4 * lg);
-        xl = mfma16(as_i16x4(al_), as_i16x4(lk), xl);
-        xh = mfma16(as_i16x4(ah_), as_i16x4(lk), xh);
-      } else {
-#pragma unroll
-        for (int kc = 0; kc < RP / 32; ++kc) {
-          const bf16x8 lk = lko32[kc];
-          const uint4 al_ = *reinterpret_cast<const uint4*>(btp + (size_t)16 * cb * RP + 32 * kc + 8 * lg);
-          const uint4 ah_ = *reinterpret_cast<const uint4*>(btp + (size_t)16 * (cb + 4) * RP + 32 * kc + 8 * lg);
-          xl = mfma32(as_bf16x8(al_), lk, xl);
-          xh = mfma32(as_bf16x8(ah_), lk, xh);
-        }
-      }
-      float y1[4], y2[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        if (a.rope) {
-          y1[jj] = xl[jj] * cs[jj] - xh[jj] * sn[jj];
-          y2[jj] = xh[jj] * cs[jj] + xl[jj] * sn[jj];
-        } else {
-          y1[jj] = xl[jj];
-          y2[jj] = xh[jj];
-        }
-      }
-      const bf16x8 yop = cat8(pack_bf16x4(y1[0], y1[1], y1[2], y1[3]), pack_bf16x4(y2[0], y2[1], y2[2], y2[3]));
-      const bool mine = fr.row_ok && (fr.row_al == al);
-      sacc = mfma32(yop, mine ? qa : zero8, sacc);
-    }
-  }
-  return sacc;
-}
-
-template <int RP>
-__device__ __forceinline__ void compute_step(const Step<RP>& s, const DecodeArgs& a, const Frame& fr,
-                                             const TileAgent* s_agent, const uint16_t* s_bt, int ns, bool shared_l,
-                                             int t_end, int lc, int lg, float& m_run, float& l_run, f32x4 (&o)[8],
-                                             f32x4 (&acl)[RP / 16]) {
-  constexpr int NRT = RP / 16;
-  const int tb = s.tb;
-  // token validity of this lane's slots: token tb + 16b + 4lg + jj
-  bool tv[2][4];
-  uint32_t m01[2], m23[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) tv[b][jj] = (tb + 16 * b + 4 * lg + jj) < t_end;
-    m01[b] = (tv[b][0] ? 0xFFFFu : 0u) | (tv[b][1] ? 0xFFFF0000u : 0u);
-    m23[b] = (tv[b][2] ? 0xFFFFu : 0u) | (tv[b][3] ? 0xFFFF0000u : 0u);
-  }
-  const bf16x8 zero8 = as_bf16x8(make_uint4(0, 0, 0, 0));
-
-  // ---- scores S^T, one block after the other ----
-  f32x4 sacc[2];
-  sacc[0] = block_scores<RP>(s, 0, a, fr, s_agent, s_bt, ns, shared_l, lc, lg);
-  sacc[1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (s.nblk > 1) sacc[1] = block_scores<RP>(s, 1, a, fr, s_agent, s_bt, ns, shared_l, lc, lg);
-
-  // ---- online softmax over this step's 32 tokens (base-2 domain) ----
-  float sv[2][4];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      sv[b][jj] = tv[b][jj] ? sacc[b][jj] * a.sm_scale_log2 : -INFINITY;
-      mx = fmaxf(mx, sv[b][jj]);
-    }
-  mx = wave_max_across_groups(mx);
-  const float m_new = fmaxf(m_run, mx);
-  const float alpha = fast_exp2(m_run - m_new);
-  float p[2][4];
-  float psum = 0.f;
-#pragma unroll
-  for (int b = 0; b < 2; ++b)
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      p[b][jj] = fast_exp2(sv[b][jj] - m_new);
-      psum += p[b][jj];
-    }
-  l_run = l_run * alpha + psum;
-  m_run = m_new;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] *= alpha;
-#pragma unroll
-  for (int i = 0; i < NRT; ++i) acl[i] *= alpha;
-
-  // P^T operand: slots 0..3 = block 0 tokens 4lg+jj, slots 4..7 = block 1
-  const bf16x8 pop = cat8(pack_bf16x4(p[0][0], p[0][1], p[0][2], p[0][3]), pack_bf16x4(p[1][0], p[1][1], p[1][2], p[1][3]));
-  // NaN-safe: value rows of positions past the end are selected to zero
-#pragma unroll
-  for (int cb = 0; cb < 8; ++cb) {
-    const uint2 v0 = make_uint2(s.vr[0][cb].x & m01[0], s.vr[0][cb].y & m23[0]);
-    const uint2 v1 = make_uint2(s.vr[1][cb].x & m01[1], s.vr[1][cb].y & m23[1]);
-    o[cb] = mfma32(cat8(v0, v1), pop, o[cb]);
-  }
-
-  // C^T += L_v^T P^T (per agent pool; rows of other agents masked out)
-  for (int al = 0; al < ns; ++al) {
-    if (shared_l && al > 0) break;
-    const TileAgent& ag = s_agent[al];
-    const bf16x8 pm = (shared_l || (fr.row_ok && fr.row_al == al)) ? pop : zero8;
-#pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) {
-      uint2 lvr[2];
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (Step<RP>::kLv && al == 0) {
-          lvr[b] = s.lv[b][Step<RP>::kLv ? rr : 0];
-        } else {
-          lvr[b] = b < s.nblk ? load_lv(ag, s.phys[b], rr, lc, lg) : make_uint2(0, 0);
-        }
-        lvr[b].x &= m01[b];
-        lvr[b].y &= m23[b];
-      }
-      acl[rr] = mfma32(cat8(lvr[0], lvr[1]), pm, acl[rr]);
-    }
-  }
-}
 
 struct WorkItem {
   int g, rt, h, c, s_first, s0, ns, T, nact, t_begin, t_end, tile_id;
@@ -338,48 +101,44 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, bo
   }
   w.rt = rem % a.row_tiles;
   w.g = rem / a.row_tiles;
-  w.s_first = a.group_offsets ? a.group_offsets[w.g] : w.g;
-  const int s_end = a.group_offsets ? a.group_offsets[w.g + 1] : w.g + 1;
+  w.s_first = a.group_offsets ? sload(a.group_offsets + w.g) : w.g;
+  const int s_end = a.group_offsets ? sload(a.group_offsets + w.g + 1) : w.g + 1;
   w.s0 = w.s_first + w.rt * a.apt;
   w.ns = min(a.apt, s_end - w.s0);
   w.tile_id = (w.g * a.row_tiles + w.rt) * a.Hkv + w.h;
   if (w.ns <= 0) return false;
-  w.T = a.context_lens[w.s_first];
+  w.T = sload(a.context_lens + w.s_first);
   w.nact = (w.T + a.split - 1) / a.split;
   w.t_begin = w.c * a.split;
   w.t_end = min(w.T, w.t_begin + a.split);
   return true;
 }
 
-__device__ __forceinline__ TileAgent tile_agent(const DecodeArgs& a, int seq) {
-  const int ag = a.agent_ids[seq];
-  TileAgent t;
-  t.lk = (const uint16_t*)a.lk[ag];
-  t.lv = (const uint16_t*)a.lv[ag];
-  t.bk = (const uint16_t*)a.bk[ag];
-  t.bv = (const uint16_t*)a.bv[ag];
-  t.r = a.ranks[ag];
-  t.seq = seq;
-  return t;
-}
-
 // Main kernel: one workgroup of kDecodeWaves waves per (group, row tile,
-// split, KV head). Writes the split's partial state (m, l, O, C per row), or
-// the finished rows when the context fits one split.
-template <int RP>
+// split, KV head). NA is a compile-time bound on the agents of a row tile
+// (a tile with fewer runs with zero B_k / L rows for the missing ones).
+// Writes the split's record (m, l, seq, nact, O' per row), or the finished
+// rows when the context fits one split.
+template <int RP, int NA>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const DecodeArgs a) {
-  constexpr int NRT = RP / 16;  // 16-rank tiles of the value accumulator
-  constexpr int PW = D + RP;    // floats per merged row (O then C)
-  constexpr int PW4 = PW / 4;
+  constexpr int NRT = RP / 16;
+  constexpr int KC = RP >= 32 ? RP / 32 : 1;
+  constexpr int PW = D + RP;  // floats per row of a merged state (O then C)
   constexpr int NT = kDecodeWaves * 64;
   constexpr int HW = kDecodeWaves / 2;
+  constexpr int kBtBytes = NA * D * RP * 2;
+  constexpr int kMergeBytes = HW * 16 * PW * 4;
+  constexpr int kRegion = kBtBytes > kMergeBytes ? kBtBytes : kMergeBytes;
+  static_assert(NA * RP <= 256, "staged B_k^T / B_v^T of a tile exceed their LDS budget");
 
-  __shared__ __align__(16) unsigned char smem[kLdsMain];
-  __shared__ TileAgent s_agent[16];
-  __shared__ int s_phys[kMaxSplitBlocks];
+  __shared__ __align__(16) unsigned char s_region[kRegion];  // B_k^T [al][dim][k] in the loop, merge buffer after
+  __shared__ __align__(16) uint16_t s_bvt[NA * D * RP];      // B_v^T [al][dim][k]
+  __shared__ __align__(16) uint16_t s_q[16 * kQPitch];       // query tile [row][dim]
+  __shared__ __align__(16) float s_roff[16 * kRotPitch];     // (cos, sin) of lc theta_i, [lc][i]
+  __shared__ __align__(16) float s_rbase[kDecodeWaves][2 * kMaxRopePairs];  // per wave: (cos, sin) of tb theta_i
   __shared__ double s_rev[kMaxRopePairs];
-  __shared__ __align__(16) uint16_t s_q[16 * kQPitch];
-  __shared__ __align__(16) uint16_t s_bv[256 * D];  // [al][k][dim], apt * RP <= 256
+  __shared__ TileAgent s_agent[NA];
+  __shared__ float s_ml[2][HW][16];
   __shared__ int s_shared_l;
 
   // ---- work item; consecutive logical items are dealt to one XCD ----
@@ -406,78 +165,139 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const int HD = a.Hkv * D;
   const int* bt_row = a.block_tables + (size_t)wi.s_first * a.max_blocks;
   const int blk0 = t_begin / kBlock;
-  const int nsteps = (t_end - t_begin + kStepTokens - 1) / kStepTokens;
+  const int nb = (t_end - t_begin + kBlock - 1) / kBlock;  // cache blocks of the split
+  const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
 
-  // the first step's base K/V loads go out before anything else; the agent's
-  // pointers (a dependent chain of loads) follow
-  Step<RP> buf;
-  int st = wave;
-  if (st < nsteps) {
-    const int tb = t_begin + st * kStepTokens;
-    const int bi = tb / kBlock;
-    const int p0 = bt_row[bi];
-    const int p1 = (tb + kBlock < t_end) ? bt_row[bi + 1] : p0;
-    load_step_k(buf, a, tb, t_end, p0, p1, h, lc, lg);
-  }
-  __builtin_amdgcn_sched_barrier(0);
-  const TileAgent ag0 = tile_agent(a, s0);
-  if (st < nsteps) {
-    load_step_l(buf, ag0, lc, lg);
-    load_step_v(buf, a, h, lc, lg);
-  }
-
-  // ---- preamble: agent table, block ids of the split, B_k^T in LDS, q ----
-  if (tid < ns) s_agent[tid] = tile_agent(a, s0 + tid);
-  {
-    const int nb = (t_end - t_begin + kBlock - 1) / kBlock;
-    for (int i = tid; i < nb; i += NT) s_phys[i] = bt_row[blk0 + i];
-  }
-  if (tid < kMaxRopePairs) s_rev[tid] = a.rope_rev[tid];
-  __syncthreads();
-  if (tid == 0) {
-    int sh = 1;
-    for (int i = 1; i < ns; ++i)
-      sh &= (s_agent[i].lk == s_agent[0].lk) & (s_agent[i].lv == s_agent[0].lv) & (s_agent[i].r == s_agent[0].r);
-    s_shared_l = sh;
-  }
-  // s_bt[al][dim][k] = B_k,al[k, h*D + dim] (zero for k >= r); lanes take
-  // consecutive k so the 2-byte LDS writes of a wave fall in distinct banks
-  uint16_t* s_bt = reinterpret_cast<uint16_t*>(smem);
-  for (int e = tid; e < ns * RP * (D / 8); e += NT) {
-    const int k = e % RP;
-    const int d8 = ((e / RP) % (D / 8)) * 8;
-    const int al = e / (RP * (D / 8));
-    const TileAgent& t = s_agent[al];
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (k < t.r) v = ld16(t.bk + (size_t)k * HD + h * D + d8);
-    const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
+  // ---- loads of one block; a block past the split gets zero-length ranges
+  // (its loads return zero and touch no memory) ----
+  auto load_k = [&](Blk<RP>& B, int bi) __attribute__((always_inline)) {
+    const bool ok = bi < nb;
+    const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
+    const auto r = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
+                            ok ? kBlock * D * 2 : 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) s_bt[((size_t)al * D + d8 + i) * RP + k] = pv[i];
-  }
+    for (int ks = 0; ks < 4; ++ks) B.kr[ks] = as_bf16x8(bld16(r, (lc * D + 8 * lg + 32 * ks) * 2));
+  };
+  auto load_lv = [&](Blk<RP>& B, int bi, const uint16_t* lk0, const uint16_t* lv0, int r0)
+                     __attribute__((always_inline)) {
+    const bool ok = bi < nb;
+    const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
+    const auto rlk = buf_rsrc(lk0 + (size_t)phys * kBlock * r0, ok ? kBlock * r0 * 2 : 0);
+    if constexpr (RP == 16) {
+      B.lk16 = bld8(rlk, (4 * lg < r0) ? (lc * r0 + 4 * lg) * 2 : kOob);
+    } else {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        B.lk32[kc] = as_bf16x8(bld16(rlk, (32 * kc + 8 * lg < r0) ? (lc * r0 + 32 * kc + 8 * lg) * 2 : kOob));
+    }
+    const auto rlv = buf_rsrc(lv0 + (size_t)phys * r0 * kBlock, ok ? r0 * kBlock * 2 : 0);
+#pragma unroll
+    for (int rr = 0; rr < NRT; ++rr)
+      B.lv[rr] = bld8(rlv, (16 * rr + lc < r0) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+    const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
+                             ok ? D * kBlock * 2 : 0);
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb) B.vr[cb] = bld8(rv, ((16 * cb + lc) * kBlock + 4 * lg) * 2);
+  };
 
-  // B_v rows of head h for every agent of the tile (applied to the rank-space
-  // accumulator once per row after the token loop)
-  for (int e = tid; e < ns * RP * (D / 8); e += NT) {
-    const int al = e / (RP * (D / 8)), k = (e / (D / 8)) % RP, d8 = (e % (D / 8)) * 8;
-    const TileAgent& t = s_agent[al];
-    const uint4 v = k < t.r ? ld16(t.bv + (size_t)k * HD + h * D + d8) : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(s_bv + ((size_t)al * RP + k) * D + d8) = v;
+  // ---- (1) the rotary table (kernel arguments), then the base keys of this
+  // wave's first block; later waits for the table cover nothing else ----
+  double rev_arg = 0.0;
+  if (tid < kMaxRopePairs) rev_arg = a.rope_rev[tid];
+  __builtin_amdgcn_sched_barrier(0);
+  Blk<RP> bufA, bufB;
+  load_k(bufA, wave);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- (2) agent table, from scalar loads only (which do not wait behind
+  // the vector loads in flight) ----
+  if (wave == 0) {
+    int sh = 1;
+    const uint16_t *lk0 = nullptr, *lv0 = nullptr;
+    int r0 = 0;
+    for (int al = 0; al < NA; ++al) {
+      TileAgent t{nullptr, nullptr, nullptr, nullptr, 0, 0};
+      if (al < ns) {
+        const int seq = s0 + al;
+        const int ag = sload(a.agent_ids + seq);
+        t.lk = (const uint16_t*)sload(a.lk + ag);
+        t.lv = (const uint16_t*)sload(a.lv + ag);
+        t.bk = (const uint16_t*)sload(a.bk + ag);
+        t.bv = (const uint16_t*)sload(a.bv + ag);
+        t.r = sload(a.ranks + ag);
+        t.seq = seq;
+        if (al == 0) {
+          lk0 = t.lk;
+          lv0 = t.lv;
+          r0 = t.r;
+        } else {
+          sh &= (t.lk == lk0) & (t.lv == lv0) & (t.r == r0);
+        }
+      }
+      if (lane == 0) s_agent[al] = t;
+    }
+    if (lane == 0) s_shared_l = sh;
   }
-  // query tile: row r = (agent slot r / G, head r % G); rows past the tile are zero
-  for (int e = tid; e < 16 * (D / 8); e += NT) {
-    const int r = e / (D / 8), d8 = (e % (D / 8)) * 8;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r / G < ns && r < a.apt * G) v = ld16((const uint16_t*)a.q + ((size_t)(s0 + r / G) * a.Hq + h * G + (r % G)) * D + d8);
-    *reinterpret_cast<uint4*>(s_q + r * kQPitch + d8) = v;
+  if (tid < kMaxRopePairs) s_rev[tid] = rev_arg;
+  __syncthreads();
+
+  // ---- (3) staging loads: B_k, B_v rows of head h per agent, the query tile ----
+  constexpr int kItemsB = NA * RP * (D / 8);  // 8-dim chunks of B_k (and of B_v)
+  constexpr int kPerB = (kItemsB + NT - 1) / NT;
+  uint4 stk[kPerB], stv[kPerB];
+#pragma unroll
+  for (int i = 0; i < kPerB; ++i) {
+    const int e = tid + i * NT;
+    const int k = e % RP, d8 = ((e / RP) % (D / 8)) * 8, al = (e / (RP * (D / 8))) % NA;
+    stk[i] = make_uint4(0, 0, 0, 0);
+    stv[i] = make_uint4(0, 0, 0, 0);
+    if (e < kItemsB && k < s_agent[al].r) {
+      stk[i] = ld16(s_agent[al].bk + (size_t)k * HD + h * D + d8);
+      stv[i] = ld16(s_agent[al].bv + (size_t)k * HD + h * D + d8);
+    }
   }
-  Frame fr;
-  fr.rev = s_rev;
-  fr.q = s_q + lc * kQPitch;
-  fr.row_al = lc / G;
-  fr.row_ok = (fr.row_al < ns) && (lc < a.apt * G);
+  uint4 stq = make_uint4(0, 0, 0, 0);
+  const int qrow = tid / (D / 8), qd8 = (tid % (D / 8)) * 8;
+  if (tid < 16 * (D / 8) && qrow / G < ns && qrow < a.apt * G)
+    stq = ld16((const uint16_t*)a.q + ((size_t)(s0 + qrow / G) * a.Hq + h * G + (qrow % G)) * D + qd8);
+
+  // ---- (4) the rest of the first block ----
+  const uint16_t* lk0 = uniform_ptr(s_agent[0].lk);
+  const uint16_t* lv0 = uniform_ptr(s_agent[0].lv);
+  const int r0 = uniform(s_agent[0].r);
+  load_lv(bufA, wave, lk0, lv0, r0);
+
+  // ---- (5) staged values into LDS (waits for the first keys and the
+  // staging loads, not for the loads of step 4) ----
+  uint16_t* s_bt = reinterpret_cast<uint16_t*>(s_region);
+#pragma unroll
+  for (int i = 0; i < kPerB; ++i) {
+    const int e = tid + i * NT;
+    if (e < kItemsB) {
+      const int k = e % RP, d8 = ((e / RP) % (D / 8)) * 8, al = e / (RP * (D / 8));
+      const uint16_t* pk = reinterpret_cast<const uint16_t*>(&stk[i]);
+      const uint16_t* pv = reinterpret_cast<const uint16_t*>(&stv[i]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        s_bt[((size_t)al * D + d8 + j) * RP + k] = pk[j];
+        s_bvt[((size_t)al * D + d8 + j) * RP + k] = pv[j];
+      }
+    }
+  }
+  if (tid < 16 * (D / 8)) *reinterpret_cast<uint4*>(s_q + qrow * kQPitch + qd8) = stq;
+  // per-column rotation table: entries (lc, i) for lc < 16, i < 64
+  for (int e = tid; e < 16 * kMaxRopePairs; e += NT) {
+    const int col = e / kMaxRopePairs, i = e % kMaxRopePairs;
+    *reinterpret_cast<float2*>(s_roff + col * kRotPitch + 2 * i) = cos_sin_rev((double)col * s_rev[i]);
+  }
   __syncthreads();
 
   const bool shared_l = s_shared_l != 0;
+  const int row_al = lc / G;  // agent slot of this lane's query row
+  const bool row_ok = row_al < ns && lc < a.apt * G;
+  const uint16_t* qrow_p = s_q + lc * kQPitch;
+  const double rev_lane = s_rev[lane];
+
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[8];
   f32x4 acl[NRT];
@@ -486,222 +306,390 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 #pragma unroll
   for (int i = 0; i < NRT; ++i) acl[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // ---- main loop over this wave's steps ----
-  for (; st < nsteps; st += kDecodeWaves) {
-    if (st != wave) {
-      const int tb = t_begin + st * kStepTokens;
-      const int bi = tb / kBlock - blk0;
-      load_step_k(buf, a, tb, t_end, s_phys[bi], (tb + kBlock < t_end) ? s_phys[bi + 1] : 0, h, lc, lg);
-      load_step_l(buf, ag0, lc, lg);
-      load_step_v(buf, a, h, lc, lg);
+  // ---- one block: scores, online softmax, P V and P L_v ----
+  auto compute = [&](const Blk<RP>& B, int bi) __attribute__((always_inline)) {
+    const int tb = t_begin + bi * kBlock;
+    bool tv[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) tv[jj] = (tb + 4 * lg + jj) < t_end;
+    const uint32_t m01 = (tv[0] ? 0xFFFFu : 0u) | (tv[1] ? 0xFFFF0000u : 0u);
+    const uint32_t m23 = (tv[2] ? 0xFFFFu : 0u) | (tv[3] ? 0xFFFF0000u : 0u);
+
+    // low-rank key operands of every agent of the tile
+    uint2 lk16[NA];
+    bf16x8 lk32[NA][KC];
+#pragma unroll
+    for (int al = 0; al < NA; ++al) {
+      if (al == 0 || shared_l) {
+        lk16[al] = B.lk16;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) lk32[al][kc] = B.lk32[kc];
+      } else {
+        const int phys = sload(bt_row + blk0 + bi);
+        const int ra = uniform(s_agent[al].r);
+        const auto rl = buf_rsrc(uniform_ptr(s_agent[al].lk) + (size_t)phys * kBlock * ra, kBlock * ra * 2);
+        if constexpr (RP == 16) {
+          lk16[al] = bld8(rl, (4 * lg < ra) ? (lc * ra + 4 * lg) * 2 : kOob);
+        } else {
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            lk32[al][kc] = as_bf16x8(bld16(rl, (32 * kc + 8 * lg < ra) ? (lc * ra + 32 * kc + 8 * lg) * 2 : kOob));
+        }
+      }
     }
-    compute_step(buf, a, fr, s_agent, s_bt, ns, shared_l, t_end, lc, lg, m_run, l_run, o, acl);
+    // base scores
+    f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      sb = mfma32(B.kr[ks], as_bf16x8(*reinterpret_cast<const uint4*>(qrow_p + 32 * ks + 8 * lg)), sb);
+    // adapter scores: one accumulator per agent with the full query tile; each
+    // row then takes its own agent's accumulator
+    f32x4 sa[NA];
+#pragma unroll
+    for (int al = 0; al < NA; ++al) sa[al] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto adapter = [&](auto rope_tag) __attribute__((always_inline)) {
+      constexpr bool ROPE = decltype(rope_tag)::value;
+      if constexpr (ROPE) {
+        // per-block part of the angles: pair `lane` at position tb
+        *reinterpret_cast<float2*>(&s_rbase[wave][2 * lane]) = cos_sin_rev((double)tb * rev_lane);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+#pragma unroll 1
+      for (int cb = 0; cb < 4; ++cb) {
+        const bf16x8 qa = cat8(*reinterpret_cast<const uint2*>(qrow_p + 16 * cb + 4 * lg),
+                               *reinterpret_cast<const uint2*>(qrow_p + 64 + 16 * cb + 4 * lg));
+        // angles of pairs 16cb + 4lg + jj at position tb + lc, by angle addition
+        float cs[4], sn[4];
+        if constexpr (ROPE) {
+          const float* pb = &s_rbase[wave][2 * (16 * cb + 4 * lg)];
+          const float* po = s_roff + lc * kRotPitch + 2 * (16 * cb + 4 * lg);
+          const float4 b01 = *reinterpret_cast<const float4*>(pb), b23 = *reinterpret_cast<const float4*>(pb + 4);
+          const float4 o01 = *reinterpret_cast<const float4*>(po), o23 = *reinterpret_cast<const float4*>(po + 4);
+          const float cB[4] = {b01.x, b01.z, b23.x, b23.z}, sB[4] = {b01.y, b01.w, b23.y, b23.w};
+          const float cO[4] = {o01.x, o01.z, o23.x, o23.z}, sO[4] = {o01.y, o01.w, o23.y, o23.w};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            cs[jj] = cB[jj] * cO[jj] - sB[jj] * sO[jj];
+            sn[jj] = sB[jj] * cO[jj] + cB[jj] * sO[jj];
+          }
+        }
+#pragma unroll
+        for (int al = 0; al < NA; ++al) {
+          const uint16_t* btp = s_bt + ((size_t)al * D + lc) * RP;
+          f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (RP == 16) {
+            const uint2 al_ = *reinterpret_cast<const uint2*>(btp + 16 * cb * RP + 4 * lg);
+            const uint2 ah_ = *reinterpret_cast<const uint2*>(btp + 16 * (cb + 4) * RP + 4 * lg);
+            xl = mfma16(as_i16x4(al_), as_i16x4(lk16[al]), xl);
+            xh = mfma16(as_i16x4(ah_), as_i16x4(lk16[al]), xh);
+          } else {
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+              const uint4 al_ = *reinterpret_cast<const uint4*>(btp + 16 * cb * RP + 32 * kc + 8 * lg);
+              const uint4 ah_ = *reinterpret_cast<const uint4*>(btp + 16 * (cb + 4) * RP + 32 * kc + 8 * lg);
+              xl = mfma32(as_bf16x8(al_), lk32[al][kc], xl);
+              xh = mfma32(as_bf16x8(ah_), lk32[al][kc], xh);
+            }
+          }
+          float y1[4], y2[4];
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            if constexpr (ROPE) {
+              y1[jj] = xl[jj] * cs[jj] - xh[jj] * sn[jj];
+              y2[jj] = xh[jj] * cs[jj] + xl[jj] * sn[jj];
+            } else {
+              y1[jj] = xl[jj];
+              y2[jj] = xh[jj];
+            }
+          }
+          const bf16x8 yop =
+              cat8(pack_bf16x4(y1[0], y1[1], y1[2], y1[3]), pack_bf16x4(y2[0], y2[1], y2[2], y2[3]));
+          sa[al] = mfma32(yop, qa, sa[al]);
+        }
+      }
+    };
+    if (a.rope)
+      adapter(std::true_type{});
+    else
+      adapter(std::false_type{});
+    f32x4 sad = sa[0];
+#pragma unroll
+    for (int al = 1; al < NA; ++al)
+      if (row_al == al) sad = sa[al];
+    // online softmax over the block's 16 tokens (base-2 domain)
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      sv[jj] = tv[jj] ? (sb[jj] + sad[jj]) * a.sm_scale_log2 : -INFINITY;
+      mx = fmaxf(mx, sv[jj]);
+    }
+    mx = wave_max_across_groups(mx);
+    const float m_new = fmaxf(m_run, mx);  // every block holds at least one valid token
+    const float alpha = fast_exp2(m_run - m_new);
+    float p[4];
+    float psum = 0.f;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      p[jj] = fast_exp2(sv[jj] - m_new);
+      psum += p[jj];
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= alpha;
+#pragma unroll
+      for (int i = 0; i < NRT; ++i) acl[i] *= alpha;
+    }
+    // P^T operand: k slots 0..3 = tokens 4lg + jj
+    const uint2 pop = pack_bf16x4(p[0], p[1], p[2], p[3]);
+    // NaN-safe: value rows of positions past the end are selected to zero
+#pragma unroll
+    for (int cb = 0; cb < 8; ++cb)
+      o[cb] = mfma16(as_i16x4(make_uint2(B.vr[cb].x & m01, B.vr[cb].y & m23)), as_i16x4(pop), o[cb]);
+    // C^T += L_v^T P^T (per agent pool; rows of other agents masked out)
+#pragma unroll
+    for (int al = 0; al < NA; ++al) {
+      if (al > 0 && shared_l) break;
+      const uint2 pm = (shared_l || (row_ok && row_al == al)) ? pop : make_uint2(0, 0);
+      uint2 lvr[NRT];
+      if (al == 0) {
+#pragma unroll
+        for (int rr = 0; rr < NRT; ++rr) lvr[rr] = B.lv[rr];
+      } else {
+        const int phys = sload(bt_row + blk0 + bi);
+        const int ra = uniform(s_agent[al].r);
+        const auto rl = buf_rsrc(uniform_ptr(s_agent[al].lv) + (size_t)phys * ra * kBlock, ra * kBlock * 2);
+#pragma unroll
+        for (int rr = 0; rr < NRT; ++rr)
+          lvr[rr] = bld8(rl, (16 * rr + lc < ra) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+      }
+#pragma unroll
+      for (int rr = 0; rr < NRT; ++rr)
+        acl[rr] = mfma16(as_i16x4(make_uint2(lvr[rr].x & m01, lvr[rr].y & m23)), as_i16x4(pm), acl[rr]);
+    }
+  };
+
+  // ---- main loop: this wave's blocks wave, wave + 8, ...; two in flight.
+  // The second block is requested only now: with every wave's whole split
+  // requested at once, the first block would arrive no earlier than the last.
+  if (wave + kDecodeWaves < nb) {
+    load_k(bufB, wave + kDecodeWaves);
+    load_lv(bufB, wave + kDecodeWaves, lk0, lv0, r0);
+  }
+  for (int bi = wave; bi < nb; bi += 2 * kDecodeWaves) {
+    compute(bufA, bi);
+    if (bi + 2 * kDecodeWaves < nb) {
+      load_k(bufA, bi + 2 * kDecodeWaves);
+      load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0);
+    }
+    if (bi + kDecodeWaves >= nb) break;
+    compute(bufB, bi + kDecodeWaves);
+    if (bi + 3 * kDecodeWaves < nb) {
+      load_k(bufB, bi + 3 * kDecodeWaves);
+      load_lv(bufB, bi + 3 * kDecodeWaves, lk0, lv0, r0);
+    }
   }
 
-  // ---- merge the waves of this workgroup in LDS (two rounds) ----
+  // ---- merge the waves of this workgroup (two rounds through LDS) ----
   float l_row = wave_sum_across_groups(l_run);
-  __syncthreads();  // s_bt is dead from here on
-  float* f = reinterpret_cast<float*>(smem);
-  float* mrow = f;                // [HW][16]
-  float* lrow = f + 16 * HW;      // [HW][16]
-  float* obuf = f + 32 * HW;      // [HW][16][PW]
-  // round 1: the upper half of the waves hands its state to the lower half
+  __syncthreads();  // B_k^T is dead from here on
+  float* obuf = reinterpret_cast<float*>(s_region);  // [HW][16][PW]
   if (wave >= HW) {
     const int slot = wave - HW;
     if (lg == 0) {
-      mrow[slot * 16 + lc] = m_run;
-      lrow[slot * 16 + lc] = l_row;
+      s_ml[0][slot][lc] = m_run;
+      s_ml[1][slot][lc] = l_row;
     }
     float* ob = obuf + ((size_t)slot * 16 + lc) * PW;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+    for (int cb = 0; cb < 8; ++cb) *reinterpret_cast<f32x4*>(ob + 16 * cb + 4 * lg) = o[cb];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ob[16 * cb + 4 * lg + jj] = o[cb][jj];
-#pragma unroll
-    for (int rr = 0; rr < NRT; ++rr)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ob[D + 16 * rr + 4 * lg + jj] = acl[rr][jj];
+    for (int rr = 0; rr < NRT; ++rr) *reinterpret_cast<f32x4*>(ob + D + 16 * rr + 4 * lg) = acl[rr];
   }
   __syncthreads();
   if (wave < HW) {
-    const float m2 = mrow[wave * 16 + lc], l2 = lrow[wave * 16 + lc];
+    const float m2 = s_ml[0][wave][lc], l2 = s_ml[1][wave][lc];
     const float mm = fmaxf(m_run, m2);
     const float w1 = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
     const float w2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mm);
-    const float* ob = obuf + ((size_t)wave * 16 + lc) * PW;
-#pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) o[cb][jj] = w1 * o[cb][jj] + w2 * ob[16 * cb + 4 * lg + jj];
-#pragma unroll
-    for (int rr = 0; rr < NRT; ++rr)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) acl[rr][jj] = w1 * acl[rr][jj] + w2 * ob[D + 16 * rr + 4 * lg + jj];
-    m_run = mm;
-    l_row = w1 * l_row + w2 * l2;
-  }
-  __syncthreads();
-  // round 2: the lower half writes, then 16 threads per row merge
-  if (wave < HW) {
-    if (lg == 0) {
-      mrow[wave * 16 + lc] = m_run;
-      lrow[wave * 16 + lc] = l_row;
-    }
     float* ob = obuf + ((size_t)wave * 16 + lc) * PW;
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+    for (int cb = 0; cb < 8; ++cb) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ob + 16 * cb + 4 * lg);
+      *reinterpret_cast<f32x4*>(ob + 16 * cb + 4 * lg) = w1 * o[cb] + w2 * v;
+    }
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ob[16 * cb + 4 * lg + jj] = o[cb][jj];
-#pragma unroll
-    for (int rr = 0; rr < NRT; ++rr)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) ob[D + 16 * rr + 4 * lg + jj] = acl[rr][jj];
-  }
-  __syncthreads();
-  const int rows_used = ns * G;
-  if (tid >= 256) return;  // 16 threads per row from here on
-  const int row = tid >> 4;
-  const int cl = tid & 15;
-  float mw[HW];
-  float Mrow = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < HW; ++w) {
-    mw[w] = mrow[w * 16 + row];
-    Mrow = fmaxf(Mrow, mw[w]);
-  }
-  float Lrow = 0.f;
-#pragma unroll
-  for (int w = 0; w < HW; ++w) {
-    mw[w] = (mw[w] == -INFINITY) ? 0.f : fast_exp2(mw[w] - Mrow);
-    Lrow += mw[w] * lrow[w * 16 + row];
-  }
-  // merged state of row `row`: O (D floats) then C (RP floats)
-  __shared__ __align__(16) float s_fin[16][PW];
-  for (int col = cl; col < PW; col += 16) {
-    float v = 0.f;
-#pragma unroll
-    for (int w = 0; w < HW; ++w) v += mw[w] * obuf[((size_t)w * 16 + row) * PW + col];
-    s_fin[row][col] = v;
-  }
-  // 16 threads of a row are consecutive lanes of one wave: a wave barrier suffices
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  const int d0 = cl * 8;
-  float acc[8];
-  int seq = 0;
-  if (row < rows_used) {
-    // O' = O + C B_v over this thread's 8 dims (B_v of the row's agent, from LDS)
-    const int al = row / G;
-    const TileAgent& ag = s_agent[al];
-    seq = ag.seq;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = s_fin[row][d0 + i];
-    for (int k = 0; k < ag.r; ++k) {
-      const uint4 bvv = *reinterpret_cast<const uint4*>(s_bv + ((size_t)al * RP + k) * D + d0);
-      const uint16_t* pb = reinterpret_cast<const uint16_t*>(&bvv);
-      const float ck = s_fin[row][D + k];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += ck * bf16_to_f32(pb[i]);
+    for (int rr = 0; rr < NRT; ++rr) {
+      const f32x4 v = *reinterpret_cast<const f32x4*>(ob + D + 16 * rr + 4 * lg);
+      *reinterpret_cast<f32x4*>(ob + D + 16 * rr + 4 * lg) = w1 * acl[rr] + w2 * v;
+    }
+    if (lg == 0) {
+      s_ml[0][wave][lc] = mm;
+      s_ml[1][wave][lc] = w1 * l_row + w2 * l2;
     }
   }
+  __syncthreads();
+
+  // ---- final merge + value adapter: wave w owns dims 16w .. 16w + 15 of all 16 rows ----
+  float wts[HW];
+  float M = -INFINITY, L = 0.f;
+#pragma unroll
+  for (int j = 0; j < HW; ++j) M = fmaxf(M, s_ml[0][j][lc]);
+#pragma unroll
+  for (int j = 0; j < HW; ++j) {
+    const float mj = s_ml[0][j][lc];
+    wts[j] = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
+    L += wts[j] * s_ml[1][j][lc];
+  }
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < HW; ++j)
+    acc += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + 16 * wave + 4 * lg);
+#pragma unroll
+  for (int rr = 0; rr < NRT; ++rr) {
+    f32x4 cm = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < HW; ++j)
+      cm += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + D + 16 * rr + 4 * lg);
+    float hi[4], lo[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      hi[jj] = bf16_to_f32((uint16_t)(pack_bf16(cm[jj], 0.f) & 0xFFFFu));
+      lo[jj] = cm[jj] - hi[jj];
+    }
+    const uint2 chi = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+    const uint2 clo = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
+#pragma unroll
+    for (int al = 0; al < NA; ++al) {
+      const bool mine = row_ok && row_al == al;
+      const uint2 bvt =
+          *reinterpret_cast<const uint2*>(s_bvt + ((size_t)al * D + 16 * wave + lc) * RP + 16 * rr + 4 * lg);
+      acc = mfma16(as_i16x4(bvt), as_i16x4(mine ? chi : make_uint2(0, 0)), acc);
+      acc = mfma16(as_i16x4(bvt), as_i16x4(mine ? clo : make_uint2(0, 0)), acc);
+    }
+  }
+  // this lane holds O'[row lc][dims 16 wave + 4lg .. +3]
+  const bool used = lc < ns * G;
+  const int seq = s_agent[row_al < NA ? row_al : 0].seq;
   if (wi.nact > 1) {
-    // partial record of this split: [m, l, seq, nact, O'[D]]; unused rows of
-    // split 0 are marked empty (nact = 0)
-    float* part = a.partials + (((size_t)wi.tile_id * a.nsplit + c) * 16 + row) * a.part_stride;
-    if (row < rows_used) {
-      if (cl == 0) *reinterpret_cast<float4*>(part) = make_float4(Mrow, Lrow, __int_as_float(seq), __int_as_float(wi.nact));
-      *reinterpret_cast<float4*>(part + 4 + d0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-      *reinterpret_cast<float4*>(part + 8 + d0) = make_float4(acc[4], acc[5], acc[6], acc[7]);
-    } else if (c == 0 && cl == 0) {
+    float* part = a.partials + (((size_t)wi.tile_id * a.nsplit + c) * 16 + lc) * a.part_stride;
+    if (used) {
+      *reinterpret_cast<f32x4*>(part + 4 + 16 * wave + 4 * lg) = acc;
+      if (wave == 0 && lg == 0)
+        *reinterpret_cast<float4*>(part) = make_float4(M, L, __int_as_float(seq), __int_as_float(wi.nact));
+    } else if (c == 0 && wave == 0 && lg == 0) {
       *reinterpret_cast<float4*>(part) = make_float4(0.f, 0.f, __int_as_float(0), __int_as_float(0));
     }
     return;
   }
   // single split: finish here (and tell the combine this row is done)
-  if (a.nsplit > 1 && cl == 0)
-    *reinterpret_cast<float4*>(a.partials + (((size_t)wi.tile_id * a.nsplit) * 16 + row) * a.part_stride) =
+  if (a.nsplit > 1 && wave == 0 && lg == 0)
+    *reinterpret_cast<float4*>(a.partials + (((size_t)wi.tile_id * a.nsplit) * 16 + lc) * a.part_stride) =
         make_float4(0.f, 0.f, __int_as_float(0), __int_as_float(1));
-  if (row < rows_used) {
-    const float inv = 1.f / Lrow;
-    uint4 ov;
-    ov.x = pack_bf16(acc[0] * inv, acc[1] * inv);
-    ov.y = pack_bf16(acc[2] * inv, acc[3] * inv);
-    ov.z = pack_bf16(acc[4] * inv, acc[5] * inv);
-    ov.w = pack_bf16(acc[6] * inv, acc[7] * inv);
-    *reinterpret_cast<uint4*>((uint16_t*)a.out + ((size_t)seq * a.Hq + h * G + (row % G)) * D + d0) = ov;
+  if (used) {
+    const float inv = 1.f / L;
+    *reinterpret_cast<uint2*>((uint16_t*)a.out + ((size_t)seq * a.Hq + h * G + (lc % G)) * D + 16 * wave + 4 * lg) =
+        pack_bf16x4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
   }
 }
 
 // Combine kernel: one wave per (group, row tile, KV head, row) merges the
 // split records of that row with weights 2^(m_c - M) and writes the output.
-// Every load goes out at once; the record of split 0 says how many splits
-// the row has (0: no such row; 1: finished by the main kernel).
-__global__ __launch_bounds__(256) void decode_bf16_combine(const DecodeArgs a) {
-  __shared__ __align__(16) float s_w[4][kMaxSplits];
-  const int wave = uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int gid = blockIdx.x * (blockDim.x >> 6) + wave;
-  const int n_tiles = a.num_groups * a.row_tiles * a.Hkv;
-  if (gid >= n_tiles * 16) return;
+// The record of split 0 says how many splits the row has (0: no such row;
+// 1: finished by the main kernel). Lanes 0..31 take the even splits, lanes
+// 32..63 the odd ones, 4 output dims per lane; every load goes out at once
+// and loads past the records read zero through the buffer range check.
+__global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
+  __shared__ float s_w[kMaxSplits];
+  const int lane = threadIdx.x;
+  const int gid = blockIdx.x;
+  const int n_rows = a.num_groups * a.row_tiles * a.Hkv * 16;
+  if (gid >= n_rows) return;
   const int tile_id = gid / 16, row = gid % 16;
   const int h = tile_id % a.Hkv;
+  const int cstride = 16 * a.part_stride;  // floats from one split's record of this row to the next
   const float* pb = a.partials + ((size_t)tile_id * a.nsplit * 16 + row) * a.part_stride;
-  const size_t cstride = (size_t)16 * a.part_stride;
-  float4 hd = make_float4(-INFINITY, 0.f, 0.f, 0.f);
-  if (lane < a.nsplit) hd = ldf4(pb + lane * cstride);
-  float4 v[kMaxSplits];
+  const auto rs = buf_rsrc(pb, ((a.nsplit - 1) * cstride + a.part_stride) * 4);
+  const uint4 hu = bld16(rs, lane < a.nsplit ? lane * cstride * 4 : kOob);
+  const int half = lane >> 5, d4 = lane & 31;
+  uint4 v[kMaxSplits / 2];
 #pragma unroll
-  for (int u = 0; u < kMaxSplits; ++u)
-    v[u] = (u < a.nsplit && lane < D / 4) ? ldf4(pb + u * cstride + 4 + 4 * lane) : make_float4(0.f, 0.f, 0.f, 0.f);
-  const int nact = __float_as_int(__shfl(hd.w, 0));
-  const int seq = __float_as_int(__shfl(hd.z, 0));
+  for (int u = 0; u < kMaxSplits / 2; ++u) {
+    const int c = 2 * u + half;
+    v[u] = bld16(rs, c < a.nsplit ? (c * cstride + 4 + 4 * d4) * 4 : kOob);
+  }
+  const int nact = __builtin_amdgcn_readfirstlane((int)hu.w);
+  const int seq = __builtin_amdgcn_readfirstlane((int)hu.z);
   if (nact <= 1) return;
   const bool okc = lane < nact;
-  float M = okc ? hd.x : -INFINITY;
+  const float m_c = __uint_as_float(hu.x), l_c = __uint_as_float(hu.y);
+  float M = okc ? m_c : -INFINITY;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  const float w = okc ? fast_exp2(hd.x - M) : 0.f;
-  float L = okc ? w * hd.y : 0.f;
+  const float w = okc ? fast_exp2(m_c - M) : 0.f;
+  float L = okc ? w * l_c : 0.f;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-  s_w[wave][lane] = w;
+  s_w[lane] = w;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < kMaxSplits; ++u) {
-    if (u < nact) {  // selected, not multiplied: records past nact may hold anything
-      const float wu = s_w[wave][u];
-      acc.x += wu * v[u].x;
-      acc.y += wu * v[u].y;
-      acc.z += wu * v[u].z;
-      acc.w += wu * v[u].w;
+  for (int u = 0; u < kMaxSplits / 2; ++u) {
+    const int c = 2 * u + half;
+    if (2 * u < nact) {  // uniform; records past nact are selected away, never multiplied
+      const float wu = c < nact ? s_w[c] : 0.f;
+      const uint32_t* vv = reinterpret_cast<const uint32_t*>(&v[u]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += c < nact ? wu * __uint_as_float(vv[i]) : 0.f;
     }
   }
-  if (lane < D / 4) {
-    const float inv = 1.f / L;
-    const uint2 ov = make_uint2(pack_bf16(acc.x * inv, acc.y * inv), pack_bf16(acc.z * inv, acc.w * inv));
-    *reinterpret_cast<uint2*>((uint16_t*)a.out + ((size_t)seq * a.Hq + h * a.G + (row % a.G)) * D + 4 * lane) = ov;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[i]), __float_as_uint(acc[i]), false, false);
+    acc[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
+  if (half == 0) {
+    const float inv = 1.f / L;
+    const uint2 ov = make_uint2(pack_bf16(acc[0] * inv, acc[1] * inv), pack_bf16(acc[2] * inv, acc[3] * inv));
+    *reinterpret_cast<uint2*>((uint16_t*)a.out + ((size_t)seq * a.Hq + h * a.G + (row % a.G)) * D + 4 * d4) = ov;
+  }
+}
+
+template <int RP, int NA>
+void launch_main(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_bf16_kernel<RP, NA>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
 }
 
 }  // namespace
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, hipStream_t stream) {
+hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t stream) {
   const int per = (a.n_work + kNumXcd - 1) / kNumXcd;
-  const dim3 grid(per * kNumXcd), block(kDecodeWaves * 64);
+  const dim3 grid(per * kNumXcd);
   const int n_rows = a.num_groups * a.row_tiles * a.Hkv * 16;
-  const dim3 cgrid((n_rows + 3) / 4), cblock(256);
-  switch (rp) {
-    case 16: hipLaunchKernelGGL(decode_bf16_kernel<16>, grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(decode_bf16_kernel<32>, grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL(decode_bf16_kernel<64>, grid, block, 0, stream, a); break;
+  switch (rp * 100 + na) {
+    case 1601: launch_main<16, 1>(a, grid, stream); break;
+    case 1602: launch_main<16, 2>(a, grid, stream); break;
+    case 1604: launch_main<16, 4>(a, grid, stream); break;
+    case 1608: launch_main<16, 8>(a, grid, stream); break;
+    case 1616: launch_main<16, 16>(a, grid, stream); break;
+    case 3201: launch_main<32, 1>(a, grid, stream); break;
+    case 3202: launch_main<32, 2>(a, grid, stream); break;
+    case 3204: launch_main<32, 4>(a, grid, stream); break;
+    case 3208: launch_main<32, 8>(a, grid, stream); break;
+    case 6401: launch_main<64, 1>(a, grid, stream); break;
+    case 6402: launch_main<64, 2>(a, grid, stream); break;
+    case 6404: launch_main<64, 4>(a, grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit <= 1) return e;
-  hipLaunchKernelGGL(decode_bf16_combine, cgrid, cblock, 0, stream, a);
+  hipLaunchKernelGGL(decode_bf16_combine, dim3(n_rows), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -78,6 +78,15 @@ __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Load of a value that is the same for the whole wave from memory the kernel
+// never writes: read through the constant address space, so a wave-uniform
+// address becomes a scalar load (counted apart from the vector loads in
+// flight, so waiting for it never waits for them).
+template <typename T>
+__device__ __forceinline__ T sload(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)(p);
+}
+
 // Reductions over the 4 rows of 16 lanes (lanes l, l^16, l^32, l^48) that
 // hold the same accumulator column, with the gfx950 row-swap moves (plain
 // VALU data movement, no LDS round trip). Each step combines a lane's value

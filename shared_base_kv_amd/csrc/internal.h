@@ -12,7 +12,7 @@ constexpr int kBlock = 16;       // tokens per cache block
 constexpr int kNumCU = 256;      // MI355X compute units (8 XCDs x 32)
 constexpr int kNumXcd = 8;       // workgroups are dealt round-robin over XCDs
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup
-constexpr int kStepTokens = 32;  // tokens per wave step (two cache blocks)
+constexpr int kWaveBlocks = 2;   // cache blocks per wave in the smallest split
 constexpr int kMaxSplits = 64;   // split-K partitions per (group, head, row tile)
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxSplitBlocks = 256;  // cache blocks in one split (split <= 4096 tokens)
@@ -24,7 +24,8 @@ struct DecodePlan {
   int apt;          // sequences of a group served by one row tile
   int row_tiles;    // row tiles per group (upper bound)
   int rp;           // rank padded to the MFMA k granule (16, 32, 64)
-  int split;        // tokens per split (multiple of kDecodeWaves * kStepTokens)
+  int na;           // power-of-two bound on the sequences of one row tile (kernel variant)
+  int split;        // tokens per split (multiple of kDecodeWaves * kWaveBlocks * kBlock)
   int nsplit;       // splits for the longest context
   int part_stride;  // floats per partial row record: 4 (m, l, seq, nact) + d
   size_t partial_bytes;
@@ -105,7 +106,7 @@ struct PrefillArgs {
   double rope_rev[kMaxRopePairs];
 };
 
-hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, hipStream_t stream);
+hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_lr_build_bf16(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

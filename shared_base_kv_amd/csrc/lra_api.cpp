@@ -54,8 +54,10 @@ DecodePlan decode_plan(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
   if (p.apt > 256 / p.rp) p.apt = 256 / p.rp;  // staged B_k^T of a tile fits 64 KB of LDS
   const int max_group = S - num_groups + 1;
   p.row_tiles = ceil_div(max_group, p.apt);
+  p.na = 1;
+  while (p.na < (max_group < p.apt ? max_group : p.apt)) p.na *= 2;
   const long long items = (long long)num_groups * p.row_tiles * Hkv;
-  const int granule = kDecodeWaves * kStepTokens;
+  const int granule = kDecodeWaves * kWaveBlocks * kBlock;
   long long split = ((long long)max_ctx * items + kNumCU - 1) / kNumCU;
   split = (long long)round_up((size_t)split, granule);
   if (split < granule) split = granule;
@@ -235,7 +237,7 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
                                          p.row_tiles * p.rp;
     a.xcd_by_head = 4 * lr_bytes_per_token <= 4LL * Hkv * d;
   }
-  const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, (hipStream_t)stream)
+  const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
                                          : launch_decode_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
   return ok();
