@@ -45,7 +45,8 @@ namespace {
 
 constexpr int D = 128;
 constexpr int kQPitch = D + 8;                    // LDS row pitch of the query tile (bf16)
-constexpr int kRotPitch = 2 * kMaxRopePairs + 4;  // LDS row pitch of the per-column rotation table (floats)
+constexpr int kRotPitch = kMaxRopePairs + 4;      // LDS row pitch of the per-column rotation table (f16 pairs)
+constexpr int kQpPitch = D + 8;                   // LDS row pitch of the permuted f16 query tile (halves)
 
 struct TileAgent {
   const uint16_t* lk;
@@ -80,6 +81,19 @@ struct Blk {
   uint2 lk16;       // L_k[token lc][ranks 4lg .. +3]              (RP 16)
   bf16x8 lk32[KC];  // L_k[token lc][ranks 32kc + 8lg .. +7]       (RP 32, 64)
   uint2 lv[NRT];    // L_v[rank 16rr + lc][tokens 4lg .. +3]
+};
+
+// Low-rank rows of agents 1 .. NA-1 of the tile for one block (agent 0's
+// travel with the block). Loaded only when the agents keep separate pools;
+// otherwise the loads get zero-length ranges.
+template <int RP, int NA>
+struct AgentRows {
+  static constexpr int KC = RP >= 32 ? RP / 32 : 1;
+  static constexpr int NRT = RP / 16;
+  static constexpr int N = NA > 1 ? NA - 1 : 1;
+  uint2 lk16[N];
+  bf16x8 lk32[N][KC];
+  uint2 lv[N][NRT];
 };
 
 struct WorkItem {
@@ -134,8 +148,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   __shared__ __align__(16) unsigned char s_region[kRegion];  // B_k^T [al][dim][k] in the loop, merge buffer after
   __shared__ __align__(16) uint16_t s_bvt[NA * D * RP];      // B_v^T [al][dim][k]
   __shared__ __align__(16) uint16_t s_q[16 * kQPitch];       // query tile [row][dim]
-  __shared__ __align__(16) float s_roff[16 * kRotPitch];     // (cos, sin) of lc theta_i, [lc][i]
-  __shared__ __align__(16) float s_rbase[kDecodeWaves][2 * kMaxRopePairs];  // per wave: (cos, sin) of tb theta_i
+  __shared__ __align__(16) uint16_t s_qp[16 * kQpPitch];     // f16 query tile, k slots of the adapter product
+  __shared__ __align__(16) f16x2 s_roff[16 * kRotPitch];     // (cos, sin) of lc theta_i, [lc][i]
+  __shared__ __align__(16) f16x2 s_rbase[kDecodeWaves][kMaxRopePairs];  // per wave: (cos, sin) of tb theta_i
   __shared__ double s_rev[kMaxRopePairs];
   __shared__ TileAgent s_agent[NA];
   __shared__ float s_ml[2][HW][16];
@@ -284,11 +299,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       }
     }
   }
-  if (tid < 16 * (D / 8)) *reinterpret_cast<uint4*>(s_q + qrow * kQPitch + qd8) = stq;
+  if (tid < 16 * (D / 8)) {
+    *reinterpret_cast<uint4*>(s_q + qrow * kQPitch + qd8) = stq;
+    // f16 copy in the k-slot order of the adapter product: for dim tile cb
+    // and k-group g, slots 2j and 2j + 1 hold dims 16cb + 4g + j and + 64
+    const uint16_t* pq = reinterpret_cast<const uint16_t*>(&stq);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int d = qd8 + j, dd = d & 63;
+      const int slot = (dd >> 4) * 32 + ((dd >> 2) & 3) * 8 + 2 * (dd & 3) + (d >> 6);
+      s_qp[qrow * kQpPitch + slot] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(pq[j]));
+    }
+  }
   // per-column rotation table: entries (lc, i) for lc < 16, i < 64
   for (int e = tid; e < 16 * kMaxRopePairs; e += NT) {
     const int col = e / kMaxRopePairs, i = e % kMaxRopePairs;
-    *reinterpret_cast<float2*>(s_roff + col * kRotPitch + 2 * i) = cos_sin_rev((double)col * s_rev[i]);
+    const float2 cs = cos_sin_rev((double)col * s_rev[i]);
+    s_roff[col * kRotPitch + i] = f16x2{(_Float16)cs.x, (_Float16)cs.y};
   }
   __syncthreads();
 
@@ -296,6 +323,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const int row_al = lc / G;  // agent slot of this lane's query row
   const bool row_ok = row_al < ns && lc < a.apt * G;
   const uint16_t* qrow_p = s_q + lc * kQPitch;
+  const uint16_t* qp_row = s_qp + lc * kQpPitch;
   const double rev_lane = s_rev[lane];
 
   float m_run = -INFINITY, l_run = 0.f;
@@ -307,7 +335,43 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   for (int i = 0; i < NRT; ++i) acl[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- one block: scores, online softmax, P V and P L_v ----
-  auto compute = [&](const Blk<RP>& B, int bi) __attribute__((always_inline)) {
+  // low-rank pools of agents 1 .. NA-1 (agent 0's when the tile shares one
+  // pool: the rows are then read again, from L2, and the data path has no
+  // select on them)
+  const uint16_t* ag_lk[NA];
+  const uint16_t* ag_lv[NA];
+  int ag_r[NA];
+#pragma unroll
+  for (int al = 0; al < NA; ++al) {
+    const int src = shared_l ? 0 : al;
+    ag_lk[al] = uniform_ptr(s_agent[src].lk);
+    ag_lv[al] = uniform_ptr(s_agent[src].lv);
+    ag_r[al] = uniform(s_agent[src].r);
+  }
+  // per-agent low-rank rows of block bi (zero-length ranges past the split)
+  auto load_agents = [&](AgentRows<RP, NA>& ar, int bi) __attribute__((always_inline)) {
+    const bool ok = bi < nb;
+    const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
+#pragma unroll
+    for (int al = 1; al < NA; ++al) {
+      const int ra = ag_r[al];
+      const auto rl = buf_rsrc(ag_lk[al] + (size_t)phys * kBlock * ra, ok ? kBlock * ra * 2 : 0);
+      if constexpr (RP == 16) {
+        ar.lk16[al - 1] = bld8(rl, (4 * lg < ra) ? (lc * ra + 4 * lg) * 2 : kOob);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          ar.lk32[al - 1][kc] =
+              as_bf16x8(bld16(rl, (32 * kc + 8 * lg < ra) ? (lc * ra + 32 * kc + 8 * lg) * 2 : kOob));
+      }
+      const auto rv = buf_rsrc(ag_lv[al] + (size_t)phys * ra * kBlock, ok ? ra * kBlock * 2 : 0);
+#pragma unroll
+      for (int rr = 0; rr < NRT; ++rr)
+        ar.lv[al - 1][rr] = bld8(rv, (16 * rr + lc < ra) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+    }
+  };
+
+  auto compute = [&](const Blk<RP>& B, const AgentRows<RP, NA>& ar, int bi) __attribute__((always_inline)) {
     const int tb = t_begin + bi * kBlock;
     bool tv[4];
 #pragma unroll
@@ -318,24 +382,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     // low-rank key operands of every agent of the tile
     uint2 lk16[NA];
     bf16x8 lk32[NA][KC];
+    lk16[0] = B.lk16;
 #pragma unroll
-    for (int al = 0; al < NA; ++al) {
-      if (al == 0 || shared_l) {
-        lk16[al] = B.lk16;
+    for (int kc = 0; kc < KC; ++kc) lk32[0][kc] = B.lk32[kc];
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) lk32[al][kc] = B.lk32[kc];
-      } else {
-        const int phys = sload(bt_row + blk0 + bi);
-        const int ra = uniform(s_agent[al].r);
-        const auto rl = buf_rsrc(uniform_ptr(s_agent[al].lk) + (size_t)phys * kBlock * ra, kBlock * ra * 2);
-        if constexpr (RP == 16) {
-          lk16[al] = bld8(rl, (4 * lg < ra) ? (lc * ra + 4 * lg) * 2 : kOob);
-        } else {
+    for (int al = 1; al < NA; ++al) {
+      lk16[al] = ar.lk16[al - 1];
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            lk32[al][kc] = as_bf16x8(bld16(rl, (32 * kc + 8 * lg < ra) ? (lc * ra + 32 * kc + 8 * lg) * 2 : kOob));
-        }
-      }
+      for (int kc = 0; kc < KC; ++kc) lk32[al][kc] = ar.lk32[al - 1][kc];
     }
     // base scores
     f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -347,32 +401,37 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     f32x4 sa[NA];
 #pragma unroll
     for (int al = 0; al < NA; ++al) sa[al] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // The rotation runs in packed f16: per pair, (u, w) = (x_i, x_i+64) goes to
+    // (u c - w s, w c + u s) in two packed operations, and the rotated pair is
+    // already the operand of the f16 adapter product (k slots paired as above).
     auto adapter = [&](auto rope_tag) __attribute__((always_inline)) {
       constexpr bool ROPE = decltype(rope_tag)::value;
       if constexpr (ROPE) {
         // per-block part of the angles: pair `lane` at position tb
-        *reinterpret_cast<float2*>(&s_rbase[wave][2 * lane]) = cos_sin_rev((double)tb * rev_lane);
+        const float2 cb_ = cos_sin_rev((double)tb * rev_lane);
+        s_rbase[wave][lane] = f16x2{(_Float16)cb_.x, (_Float16)cb_.y};
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
 #pragma unroll 1
       for (int cb = 0; cb < 4; ++cb) {
-        const bf16x8 qa = cat8(*reinterpret_cast<const uint2*>(qrow_p + 16 * cb + 4 * lg),
-                               *reinterpret_cast<const uint2*>(qrow_p + 64 + 16 * cb + 4 * lg));
-        // angles of pairs 16cb + 4lg + jj at position tb + lc, by angle addition
-        float cs[4], sn[4];
+        const f16x8 qa = __builtin_bit_cast(f16x8, *reinterpret_cast<const uint4*>(qp_row + 32 * cb + 8 * lg));
+        // angles of pairs 16cb + 4lg + jj at position tb + lc, by angle addition:
+        // (cos, sin)(B + O) = (cB, sB) cO + (sB, cB) (-sO, sO)
+        f16x2 c2[4], ns2[4];
         if constexpr (ROPE) {
-          const float* pb = &s_rbase[wave][2 * (16 * cb + 4 * lg)];
-          const float* po = s_roff + lc * kRotPitch + 2 * (16 * cb + 4 * lg);
-          const float4 b01 = *reinterpret_cast<const float4*>(pb), b23 = *reinterpret_cast<const float4*>(pb + 4);
-          const float4 o01 = *reinterpret_cast<const float4*>(po), o23 = *reinterpret_cast<const float4*>(po + 4);
-          const float cB[4] = {b01.x, b01.z, b23.x, b23.z}, sB[4] = {b01.y, b01.w, b23.y, b23.w};
-          const float cO[4] = {o01.x, o01.z, o23.x, o23.z}, sO[4] = {o01.y, o01.w, o23.y, o23.w};
+          const uint4 pbv = *reinterpret_cast<const uint4*>(&s_rbase[wave][16 * cb + 4 * lg]);
+          const uint4 pov = *reinterpret_cast<const uint4*>(s_roff + lc * kRotPitch + 16 * cb + 4 * lg);
+          const uint32_t pbw[4] = {pbv.x, pbv.y, pbv.z, pbv.w};
+          const uint32_t pow_[4] = {pov.x, pov.y, pov.z, pov.w};
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            cs[jj] = cB[jj] * cO[jj] - sB[jj] * sO[jj];
-            sn[jj] = sB[jj] * cO[jj] + cB[jj] * sO[jj];
+            const f16x2 pb = __builtin_bit_cast(f16x2, pbw[jj]);
+            const f16x2 po = __builtin_bit_cast(f16x2, pow_[jj]);
+            const f16x2 cs = pb * f16x2{po.x, po.x} + f16x2{pb.y, pb.x} * f16x2{-po.y, po.y};
+            c2[jj] = f16x2{cs.x, cs.x};
+            ns2[jj] = f16x2{-cs.y, cs.y};
           }
         }
 #pragma unroll
@@ -393,20 +452,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
               xh = mfma32(as_bf16x8(ah_), lk32[al][kc], xh);
             }
           }
-          float y1[4], y2[4];
+          f16x2 y[4];
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
-            if constexpr (ROPE) {
-              y1[jj] = xl[jj] * cs[jj] - xh[jj] * sn[jj];
-              y2[jj] = xh[jj] * cs[jj] + xl[jj] * sn[jj];
-            } else {
-              y1[jj] = xl[jj];
-              y2[jj] = xh[jj];
-            }
+            const f16x2 pr = __builtin_bit_cast(f16x2, __builtin_amdgcn_cvt_pkrtz(xl[jj], xh[jj]));
+            if constexpr (ROPE)
+              y[jj] = pr * c2[jj] + f16x2{pr.y, pr.x} * ns2[jj];
+            else
+              y[jj] = pr;
           }
-          const bf16x8 yop =
-              cat8(pack_bf16x4(y1[0], y1[1], y1[2], y1[3]), pack_bf16x4(y2[0], y2[1], y2[2], y2[3]));
-          sa[al] = mfma32(yop, qa, sa[al]);
+          const f16x8 yop = {y[0].x, y[0].y, y[1].x, y[1].y, y[2].x, y[2].y, y[3].x, y[3].y};
+          sa[al] = mfma32h(yop, qa, sa[al]);
         }
       }
     };
@@ -451,47 +507,40 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     for (int cb = 0; cb < 8; ++cb)
       o[cb] = mfma16(as_i16x4(make_uint2(B.vr[cb].x & m01, B.vr[cb].y & m23)), as_i16x4(pop), o[cb]);
     // C^T += L_v^T P^T (per agent pool; rows of other agents masked out)
-#pragma unroll
-    for (int al = 0; al < NA; ++al) {
-      if (al > 0 && shared_l) break;
-      const uint2 pm = (shared_l || (row_ok && row_al == al)) ? pop : make_uint2(0, 0);
-      uint2 lvr[NRT];
-      if (al == 0) {
-#pragma unroll
-        for (int rr = 0; rr < NRT; ++rr) lvr[rr] = B.lv[rr];
-      } else {
-        const int phys = sload(bt_row + blk0 + bi);
-        const int ra = uniform(s_agent[al].r);
-        const auto rl = buf_rsrc(uniform_ptr(s_agent[al].lv) + (size_t)phys * ra * kBlock, ra * kBlock * 2);
-#pragma unroll
-        for (int rr = 0; rr < NRT; ++rr)
-          lvr[rr] = bld8(rl, (16 * rr + lc < ra) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
-      }
+    if (shared_l) {
 #pragma unroll
       for (int rr = 0; rr < NRT; ++rr)
-        acl[rr] = mfma16(as_i16x4(make_uint2(lvr[rr].x & m01, lvr[rr].y & m23)), as_i16x4(pm), acl[rr]);
+        acl[rr] = mfma16(as_i16x4(make_uint2(B.lv[rr].x & m01, B.lv[rr].y & m23)), as_i16x4(pop), acl[rr]);
+    } else {
+#pragma unroll
+      for (int al = 0; al < NA; ++al) {
+        const uint2 pm = (row_ok && row_al == al) ? pop : make_uint2(0, 0);
+#pragma unroll
+        for (int rr = 0; rr < NRT; ++rr) {
+          const uint2 lvr = al == 0 ? B.lv[rr] : ar.lv[al > 0 ? al - 1 : 0][rr];
+          acl[rr] = mfma16(as_i16x4(make_uint2(lvr.x & m01, lvr.y & m23)), as_i16x4(pm), acl[rr]);
+        }
+      }
     }
   };
 
-  // ---- main loop: this wave's blocks wave, wave + 8, ...; two in flight.
-  // The second block is requested only now: with every wave's whole split
-  // requested at once, the first block would arrive no earlier than the last.
-  if (wave + kDecodeWaves < nb) {
-    load_k(bufB, wave + kDecodeWaves);
-    load_lv(bufB, wave + kDecodeWaves, lk0, lv0, r0);
-  }
-  for (int bi = wave; bi < nb; bi += 2 * kDecodeWaves) {
-    compute(bufA, bi);
-    if (bi + 2 * kDecodeWaves < nb) {
-      load_k(bufA, bi + 2 * kDecodeWaves);
-      load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0);
-    }
-    if (bi + kDecodeWaves >= nb) break;
-    compute(bufB, bi + kDecodeWaves);
-    if (bi + 3 * kDecodeWaves < nb) {
-      load_k(bufB, bi + 3 * kDecodeWaves);
-      load_lv(bufB, bi + 3 * kDecodeWaves, lk0, lv0, r0);
-    }
+  // ---- main loop over this wave's blocks wave, wave + 8, ...: per block,
+  // first its other agents' rows, then the next block's rows, then the
+  // compute. All loads are issued on every path (out-of-range ones read
+  // nothing), so each wait covers exactly the loads issued before them. ----
+  const int nmine = wave < nb ? (nb - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+  AgentRows<RP, NA> ar;
+  for (int k = 0; k < nmine; k += 2) {
+    const int bi = wave + k * kDecodeWaves;
+    load_agents(ar, bi);
+    load_k(bufB, bi + kDecodeWaves);
+    load_lv(bufB, bi + kDecodeWaves, lk0, lv0, r0);
+    compute(bufA, ar, bi);
+    if (k + 1 >= nmine) break;
+    load_agents(ar, bi + kDecodeWaves);
+    load_k(bufA, bi + 2 * kDecodeWaves);
+    load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0);
+    compute(bufB, ar, bi + kDecodeWaves);
   }
 
   // ---- merge the waves of this workgroup (two rounds through LDS) ----
@@ -534,7 +583,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   }
   __syncthreads();
 
-  // ---- final merge + value adapter: wave w owns dims 16w .. 16w + 15 of all 16 rows ----
+  // ---- final merge + value adapter: wave w owns dim tiles DTW w .. DTW w +
+  // DTW - 1 (16 dims each) of all 16 rows ----
+  constexpr int DTW = 8 / kDecodeWaves;
   float wts[HW];
   float M = -INFINITY, L = 0.f;
 #pragma unroll
@@ -545,10 +596,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     wts[j] = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
     L += wts[j] * s_ml[1][j][lc];
   }
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int j = 0; j < HW; ++j)
-    acc += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + 16 * wave + 4 * lg);
+  // merged rank-space accumulator C of this lane's row, as bf16 hi + lo, per rank tile
+  uint2 chi[NRT], clo[NRT];
 #pragma unroll
   for (int rr = 0; rr < NRT; ++rr) {
     f32x4 cm = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -561,39 +610,51 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       hi[jj] = bf16_to_f32((uint16_t)(pack_bf16(cm[jj], 0.f) & 0xFFFFu));
       lo[jj] = cm[jj] - hi[jj];
     }
-    const uint2 chi = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
-    const uint2 clo = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
-#pragma unroll
-    for (int al = 0; al < NA; ++al) {
-      const bool mine = row_ok && row_al == al;
-      const uint2 bvt =
-          *reinterpret_cast<const uint2*>(s_bvt + ((size_t)al * D + 16 * wave + lc) * RP + 16 * rr + 4 * lg);
-      acc = mfma16(as_i16x4(bvt), as_i16x4(mine ? chi : make_uint2(0, 0)), acc);
-      acc = mfma16(as_i16x4(bvt), as_i16x4(mine ? clo : make_uint2(0, 0)), acc);
-    }
+    chi[rr] = pack_bf16x4(hi[0], hi[1], hi[2], hi[3]);
+    clo[rr] = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
   }
-  // this lane holds O'[row lc][dims 16 wave + 4lg .. +3]
   const bool used = lc < ns * G;
   const int seq = s_agent[row_al < NA ? row_al : 0].seq;
-  if (wi.nact > 1) {
-    float* part = a.partials + (((size_t)wi.tile_id * a.nsplit + c) * 16 + lc) * a.part_stride;
-    if (used) {
-      *reinterpret_cast<f32x4*>(part + 4 + 16 * wave + 4 * lg) = acc;
-      if (wave == 0 && lg == 0)
-        *reinterpret_cast<float4*>(part) = make_float4(M, L, __int_as_float(seq), __int_as_float(wi.nact));
-    } else if (c == 0 && wave == 0 && lg == 0) {
-      *reinterpret_cast<float4*>(part) = make_float4(0.f, 0.f, __int_as_float(0), __int_as_float(0));
+  float* part = a.partials + (((size_t)wi.tile_id * a.nsplit + c) * 16 + lc) * a.part_stride;
+#pragma unroll
+  for (int dt = 0; dt < DTW; ++dt) {
+    const int cbt = DTW * wave + dt;  // dim tile 16 cbt .. 16 cbt + 15
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < HW; ++j)
+      acc += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + 16 * cbt + 4 * lg);
+#pragma unroll
+    for (int rr = 0; rr < NRT; ++rr) {
+#pragma unroll
+      for (int al = 0; al < NA; ++al) {
+        const bool mine = row_ok && row_al == al;
+        const uint2 bvt =
+            *reinterpret_cast<const uint2*>(s_bvt + ((size_t)al * D + 16 * cbt + lc) * RP + 16 * rr + 4 * lg);
+        acc = mfma16(as_i16x4(bvt), as_i16x4(mine ? chi[rr] : make_uint2(0, 0)), acc);
+        acc = mfma16(as_i16x4(bvt), as_i16x4(mine ? clo[rr] : make_uint2(0, 0)), acc);
+      }
     }
-    return;
+    // this lane holds O'[row lc][dims 16 cbt + 4lg .. +3]
+    if (wi.nact > 1) {
+      if (used) *reinterpret_cast<f32x4*>(part + 4 + 16 * cbt + 4 * lg) = acc;
+    } else if (used) {
+      const float inv = 1.f / L;
+      *reinterpret_cast<uint2*>((uint16_t*)a.out + ((size_t)seq * a.Hq + h * G + (lc % G)) * D + 16 * cbt + 4 * lg) =
+          pack_bf16x4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+    }
   }
-  // single split: finish here (and tell the combine this row is done)
-  if (a.nsplit > 1 && wave == 0 && lg == 0)
-    *reinterpret_cast<float4*>(a.partials + (((size_t)wi.tile_id * a.nsplit) * 16 + lc) * a.part_stride) =
-        make_float4(0.f, 0.f, __int_as_float(0), __int_as_float(1));
-  if (used) {
-    const float inv = 1.f / L;
-    *reinterpret_cast<uint2*>((uint16_t*)a.out + ((size_t)seq * a.Hq + h * G + (lc % G)) * D + 16 * wave + 4 * lg) =
-        pack_bf16x4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  // record header (m, l, seq, nact) of this split; unused rows of split 0 are
+  // marked empty (nact = 0), and a context that fits one split marks its
+  // rows finished (nact = 1)
+  if (wave == 0 && lg == 0) {
+    if (wi.nact > 1) {
+      if (used)
+        *reinterpret_cast<float4*>(part) = make_float4(M, L, __int_as_float(seq), __int_as_float(wi.nact));
+      else if (c == 0)
+        *reinterpret_cast<float4*>(part) = make_float4(0.f, 0.f, __int_as_float(0), __int_as_float(0));
+    } else if (a.nsplit > 1) {
+      *reinterpret_cast<float4*>(part) = make_float4(0.f, 0.f, __int_as_float(0), __int_as_float(1));
+    }
   }
 }
 
