@@ -348,30 +348,41 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     ag_lv[al] = uniform_ptr(s_agent[src].lv);
     ag_r[al] = uniform(s_agent[src].r);
   }
-  // per-agent low-rank rows of block bi (zero-length ranges past the split)
-  auto load_agents = [&](AgentRows<RP, NA>& ar, int bi) __attribute__((always_inline)) {
+  // per-agent low-rank rows of block bi (zero-length ranges past the split):
+  // key rows (K) and value rows (V) separately
+  auto load_agents = [&](AgentRows<RP, NA>& ar, int bi, bool keys, bool vals) __attribute__((always_inline)) {
     const bool ok = bi < nb;
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
 #pragma unroll
     for (int al = 1; al < NA; ++al) {
       const int ra = ag_r[al];
-      const auto rl = buf_rsrc(ag_lk[al] + (size_t)phys * kBlock * ra, ok ? kBlock * ra * 2 : 0);
-      if constexpr (RP == 16) {
-        ar.lk16[al - 1] = bld8(rl, (4 * lg < ra) ? (lc * ra + 4 * lg) * 2 : kOob);
-      } else {
+      if (keys) {
+        const auto rl = buf_rsrc(ag_lk[al] + (size_t)phys * kBlock * ra, ok ? kBlock * ra * 2 : 0);
+        if constexpr (RP == 16) {
+          ar.lk16[al - 1] = bld8(rl, (4 * lg < ra) ? (lc * ra + 4 * lg) * 2 : kOob);
+        } else {
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          ar.lk32[al - 1][kc] =
-              as_bf16x8(bld16(rl, (32 * kc + 8 * lg < ra) ? (lc * ra + 32 * kc + 8 * lg) * 2 : kOob));
+          for (int kc = 0; kc < KC; ++kc)
+            ar.lk32[al - 1][kc] =
+                as_bf16x8(bld16(rl, (32 * kc + 8 * lg < ra) ? (lc * ra + 32 * kc + 8 * lg) * 2 : kOob));
+        }
       }
-      const auto rv = buf_rsrc(ag_lv[al] + (size_t)phys * ra * kBlock, ok ? ra * kBlock * 2 : 0);
+      if (vals) {
+        const auto rv = buf_rsrc(ag_lv[al] + (size_t)phys * ra * kBlock, ok ? ra * kBlock * 2 : 0);
 #pragma unroll
-      for (int rr = 0; rr < NRT; ++rr)
-        ar.lv[al - 1][rr] = bld8(rv, (16 * rr + lc < ra) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+        for (int rr = 0; rr < NRT; ++rr)
+          ar.lv[al - 1][rr] = bld8(rv, (16 * rr + lc < ra) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+      }
     }
   };
 
-  auto compute = [&](const Blk<RP>& B, const AgentRows<RP, NA>& ar, int bi) __attribute__((always_inline)) {
+  // Other agents' rows are loaded one block ahead when they fit in 16
+  // registers; larger ones are loaded at the start of the block's compute.
+  constexpr bool kAgentAhead = (NA - 1) * (RP / 4) <= 16;
+  auto compute = [&](const Blk<RP>& B, const AgentRows<RP, NA>& ar_ahead, int bi) __attribute__((always_inline)) {
+    AgentRows<RP, NA> ar_here;
+    if constexpr (!kAgentAhead) load_agents(ar_here, bi, true, false);
+    const AgentRows<RP, NA>& ar = kAgentAhead ? ar_ahead : ar_here;
     const int tb = t_begin + bi * kBlock;
     bool tv[4];
 #pragma unroll
@@ -470,6 +481,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       adapter(std::true_type{});
     else
       adapter(std::false_type{});
+    if constexpr (!kAgentAhead) load_agents(ar_here, bi, false, true);
     f32x4 sad = sa[0];
 #pragma unroll
     for (int al = 1; al < NA; ++al)
@@ -532,12 +544,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   AgentRows<RP, NA> ar;
   for (int k = 0; k < nmine; k += 2) {
     const int bi = wave + k * kDecodeWaves;
-    load_agents(ar, bi);
+    if constexpr (kAgentAhead) load_agents(ar, bi, true, true);
     load_k(bufB, bi + kDecodeWaves);
     load_lv(bufB, bi + kDecodeWaves, lk0, lv0, r0);
     compute(bufA, ar, bi);
     if (k + 1 >= nmine) break;
-    load_agents(ar, bi + kDecodeWaves);
+    if constexpr (kAgentAhead) load_agents(ar, bi + kDecodeWaves, true, true);
     load_k(bufA, bi + 2 * kDecodeWaves);
     load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0);
     compute(bufB, ar, bi + kDecodeWaves);
