@@ -130,8 +130,13 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
  *   max_rank      (host) 1..64. d: 64 or 128 (bf16: 128). block_size: 16.
  *   sm_scale      softmax scale (usually 1/sqrt(d)).
  *   rope_theta    rotary base for the adapter key term; 0 disables it.
- *   dtype         LRA_BF16 (split-K kernel on bf16 MFMA, fp32 accumulate) or
- *                 LRA_F32 (fp32 throughout).
+ *   dtype         LRA_BF16 (split-K kernel on MFMA, fp32 accumulate) or
+ *                 LRA_F32 (fp32 throughout). With LRA_BF16 the adapter part
+ *                 of each score is taken in f16: the rebuilt adapter key
+ *                 rope(L_k B_k) is formed in fp32, converted to f16 and
+ *                 rotated in f16, and q is converted to f16 for that product;
+ *                 |q| and the rebuilt adapter-key entries must stay below
+ *                 65504 (the f16 range), else the output is undefined.
  *   workspace     at least lora_attn_decode_workspace_size(...) bytes of
  *                 device memory, 16-byte aligned; it holds fp32 split-K
  *                 partial states (per split and query row: max, sum and the

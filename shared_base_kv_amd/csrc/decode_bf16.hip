@@ -100,19 +100,15 @@ struct WorkItem {
   int g, rt, h, c, s_first, s0, ns, T, nact, t_begin, t_end, tile_id;
 };
 
-__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, bool by_head, WorkItem& w) {
+// Logical work item -> (group, row tile, split, KV head). The KV head varies
+// fastest, so the heads of one split are consecutive items and share an XCD
+// (the low-rank rows of those tokens, shared by every head, reach that L2 once).
+__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, WorkItem& w) {
   int rem = logical;
-  if (by_head) {
-    w.c = rem % a.nsplit;
-    rem /= a.nsplit;
-    w.h = rem % a.Hkv;
-    rem /= a.Hkv;
-  } else {
-    w.h = rem % a.Hkv;
-    rem /= a.Hkv;
-    w.c = rem % a.nsplit;
-    rem /= a.nsplit;
-  }
+  w.h = rem % a.Hkv;
+  rem /= a.Hkv;
+  w.c = rem % a.nsplit;
+  rem /= a.nsplit;
   w.rt = rem % a.row_tiles;
   w.g = rem / a.row_tiles;
   w.s_first = a.group_offsets ? sload(a.group_offsets + w.g) : w.g;
@@ -161,7 +157,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const int logical = (int)(blockIdx.x % kNumXcd) * per + (int)(blockIdx.x / kNumXcd);
   if (logical >= a.n_work) return;
   WorkItem wi;
-  if (!decode_item(a, logical, a.xcd_by_head, wi)) {
+  if (!decode_item(a, logical, wi)) {
     // no sequences in this row tile: split 0 marks its rows empty for the combine
     if (a.nsplit > 1 && wi.c == 0 && threadIdx.x < 16)
       *reinterpret_cast<float4*>(a.partials + (((size_t)wi.tile_id * a.nsplit) * 16 + threadIdx.x) * a.part_stride) =

@@ -61,7 +61,6 @@ struct DecodeArgs {
   int32_t n_work;  // num_groups * row_tiles * nsplit * Hkv
   float sm_scale;
   float sm_scale_log2;  // sm_scale * log2(e)
-  int32_t xcd_by_head;      // 1: the splits of one (group, row tile, head) share an XCD
   int32_t rope;             // 1: rotate the adapter key term
   double rope_rev[kMaxRopePairs];  // theta^(-2i/d) / (2 pi): revolutions per position, pair i
 };

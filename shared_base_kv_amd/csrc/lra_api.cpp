@@ -230,13 +230,6 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.rope = rope_theta > 0.f;
   rope_table(a.rope_rev, rope_theta, d);
-  {
-    // keep a head's splits on one XCD (its partials stay in that L2) unless
-    // the low-rank rows shared across heads outweigh the base rows
-    const long long lr_bytes_per_token = 4LL * (S - num_groups + 1 < p.apt ? S - num_groups + 1 : p.apt) *
-                                         p.row_tiles * p.rp;
-    a.xcd_by_head = 4 * lr_bytes_per_token <= 4LL * Hkv * d;
-  }
   const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
                                          : launch_decode_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
