@@ -331,22 +331,20 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   for (int i = 0; i < NRT; ++i) acl[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // ---- one block: scores, online softmax, P V and P L_v ----
-  // low-rank pools of agents 1 .. NA-1 (agent 0's when the tile shares one
-  // pool: the rows are then read again, from L2, and the data path has no
-  // select on them)
+  // low-rank pools of agents 1 .. NA-1
   const uint16_t* ag_lk[NA];
   const uint16_t* ag_lv[NA];
   int ag_r[NA];
 #pragma unroll
   for (int al = 0; al < NA; ++al) {
-    const int src = shared_l ? 0 : al;
-    ag_lk[al] = uniform_ptr(s_agent[src].lk);
-    ag_lv[al] = uniform_ptr(s_agent[src].lv);
-    ag_r[al] = uniform(s_agent[src].r);
+    ag_lk[al] = uniform_ptr(s_agent[al].lk);
+    ag_lv[al] = uniform_ptr(s_agent[al].lv);
+    ag_r[al] = uniform(s_agent[al].r);
   }
   // per-agent low-rank rows of block bi (zero-length ranges past the split):
   // key rows (K) and value rows (V) separately
   auto load_agents = [&](AgentRows<RP, NA>& ar, int bi, bool keys, bool vals) __attribute__((always_inline)) {
+    if (shared_l) return;  // every agent reads agent 0's rows, which travel with the block
     const bool ok = bi < nb;
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
 #pragma unroll
@@ -386,18 +384,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     const uint32_t m01 = (tv[0] ? 0xFFFFu : 0u) | (tv[1] ? 0xFFFF0000u : 0u);
     const uint32_t m23 = (tv[2] ? 0xFFFFu : 0u) | (tv[3] ? 0xFFFF0000u : 0u);
 
-    // low-rank key operands of every agent of the tile
-    uint2 lk16[NA];
-    bf16x8 lk32[NA][KC];
-    lk16[0] = B.lk16;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) lk32[0][kc] = B.lk32[kc];
-#pragma unroll
-    for (int al = 1; al < NA; ++al) {
-      lk16[al] = ar.lk16[al - 1];
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) lk32[al][kc] = ar.lk32[al - 1][kc];
-    }
     // base scores
     f32x4 sb = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -411,8 +397,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     // The rotation runs in packed f16: per pair, (u, w) = (x_i, x_i+64) goes to
     // (u c - w s, w c + u s) in two packed operations, and the rotated pair is
     // already the operand of the f16 adapter product (k slots paired as above).
-    auto adapter = [&](auto rope_tag) __attribute__((always_inline)) {
+    // SHARED: every agent's low-rank key rows are agent 0's (no copies, no
+    // selects on loaded data in that path)
+    auto adapter = [&](auto rope_tag, auto shared_tag) __attribute__((always_inline)) {
       constexpr bool ROPE = decltype(rope_tag)::value;
+      constexpr bool SHARED = decltype(shared_tag)::value;
       if constexpr (ROPE) {
         // per-block part of the angles: pair `lane` at position tb
         const float2 cb_ = cos_sin_rev((double)tb * rev_lane);
@@ -448,15 +437,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
           if constexpr (RP == 16) {
             const uint2 al_ = *reinterpret_cast<const uint2*>(btp + 16 * cb * RP + 4 * lg);
             const uint2 ah_ = *reinterpret_cast<const uint2*>(btp + 16 * (cb + 4) * RP + 4 * lg);
-            xl = mfma16(as_i16x4(al_), as_i16x4(lk16[al]), xl);
-            xh = mfma16(as_i16x4(ah_), as_i16x4(lk16[al]), xh);
+            const uint2 lkop = (SHARED || al == 0) ? B.lk16 : ar.lk16[al > 0 ? al - 1 : 0];
+            xl = mfma16(as_i16x4(al_), as_i16x4(lkop), xl);
+            xh = mfma16(as_i16x4(ah_), as_i16x4(lkop), xh);
           } else {
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
               const uint4 al_ = *reinterpret_cast<const uint4*>(btp + 16 * cb * RP + 32 * kc + 8 * lg);
               const uint4 ah_ = *reinterpret_cast<const uint4*>(btp + 16 * (cb + 4) * RP + 32 * kc + 8 * lg);
-              xl = mfma32(as_bf16x8(al_), lk32[al][kc], xl);
-              xh = mfma32(as_bf16x8(ah_), lk32[al][kc], xh);
+              const bf16x8 lkop = (SHARED || al == 0) ? B.lk32[kc] : ar.lk32[al > 0 ? al - 1 : 0][kc];
+              xl = mfma32(as_bf16x8(al_), lkop, xl);
+              xh = mfma32(as_bf16x8(ah_), lkop, xh);
             }
           }
           f16x2 y[4];
@@ -473,10 +464,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
         }
       }
     };
-    if (a.rope)
-      adapter(std::true_type{});
-    else
-      adapter(std::false_type{});
+    if (shared_l) {
+      if (a.rope)
+        adapter(std::true_type{}, std::true_type{});
+      else
+        adapter(std::false_type{}, std::true_type{});
+    } else {
+      if (a.rope)
+        adapter(std::true_type{}, std::false_type{});
+      else
+        adapter(std::false_type{}, std::false_type{});
+    }
     if constexpr (!kAgentAhead) load_agents(ar_here, bi, false, true);
     f32x4 sad = sa[0];
 #pragma unroll
@@ -543,11 +541,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     if constexpr (kAgentAhead) load_agents(ar, bi, true, true);
     load_k(bufB, bi + kDecodeWaves);
     load_lv(bufB, bi + kDecodeWaves, lk0, lv0, r0);
+    __builtin_amdgcn_sched_barrier(0);  // nothing of the compute moves above these loads
     compute(bufA, ar, bi);
     if (k + 1 >= nmine) break;
     if constexpr (kAgentAhead) load_agents(ar, bi + kDecodeWaves, true, true);
     load_k(bufA, bi + 2 * kDecodeWaves);
     load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0);
+    __builtin_amdgcn_sched_barrier(0);
     compute(bufB, ar, bi + kDecodeWaves);
   }
 
