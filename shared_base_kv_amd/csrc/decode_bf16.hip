@@ -45,6 +45,7 @@ namespace {
 
 constexpr int D = 128;
 constexpr int kQPitch = D + 8;                    // LDS row pitch of the query tile (bf16)
+constexpr float kMaxSlack = 8.f;                  // log2 of the largest probability kept before a rescale
 constexpr int kRotPitch = kMaxRopePairs + 4;      // LDS row pitch of the per-column rotation table (f16 pairs)
 constexpr int kQpPitch = D + 8;                   // LDS row pitch of the permuted f16 query tile (halves)
 
@@ -489,8 +490,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       mx = fmaxf(mx, sv[jj]);
     }
     mx = wave_max_across_groups(mx);
-    const float m_new = fmaxf(m_run, mx);  // every block holds at least one valid token
-    const float alpha = fast_exp2(m_run - m_new);
+    // The reference max moves only when the block exceeds it by more than
+    // kMaxSlack (base 2), so most blocks need no rescale; probabilities stay
+    // below 2^kMaxSlack and l, O and C share the reference. Every block holds
+    // at least one valid token, so the first block always moves it.
+    const float m_cand = fmaxf(m_run, mx);
+    const bool move = m_cand > m_run + kMaxSlack;
+    const float m_new = move ? m_cand : m_run;
+    const float alpha = move ? fast_exp2(m_run - m_new) : 1.f;
     float p[4];
     float psum = 0.f;
 #pragma unroll

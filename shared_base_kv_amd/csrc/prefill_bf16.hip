@@ -49,6 +49,7 @@ constexpr int kKPitch = D + 8;          // LDS row pitch of the key tile (bf16)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
 constexpr int kKBufs = 2;
 constexpr int kVBufs = 3;
+constexpr float kMaxSlack = 8.f;  // log2 of the largest probability kept before a rescale
 
 // (cos, sin) of one angle given in revolutions, with the revolution count
 // reduced exactly in fp64 first.
@@ -368,10 +369,15 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
           mx = fmaxf(mx, sacc[kb][rt][jj]);
         }
       mx = wave_max_across_groups(mx);
-      const float m_new = fmaxf(m_run[rt], mx * csc);
+      // The reference max of a row moves only when the tile exceeds it by more
+      // than kMaxSlack (base 2), so most tiles need no rescale; probabilities
+      // stay below 2^kMaxSlack, and l and O use the same reference.
+      const float m_cand = fmaxf(m_run[rt], mx * csc);
+      const bool move = m_cand > m_run[rt] + kMaxSlack;  // always on a row's first visible key
+      const float m_new = move ? m_cand : m_run[rt];
       // with MASK a row may have seen no key yet (m_new = -inf): keep its state
       const bool dead = MASK && m_new == -INFINITY;
-      alpha[rt] = dead ? 1.f : fast_exp2(m_run[rt] - m_new);
+      alpha[rt] = move ? fast_exp2(m_run[rt] - m_new) : 1.f;
       const float nm = dead ? 0.f : -m_new;
       float psum = 0.f;
       float pv_[4][4];
