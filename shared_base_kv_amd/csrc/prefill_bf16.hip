@@ -14,9 +14,13 @@
 //     space, and C B_v is applied once per row after the key loop.
 //
 // Work decomposition: one workgroup = (sequence s, KV head h, query tile);
-// a query tile has 128 rows = 128/G query tokens x G query heads, 4 waves of
-// 32 rows. All tiles of one KV head are dealt to one XCD, so the keys they
-// share (the common prefix) stream through one L2.
+// a query tile has 128 rows = 128/G query tokens x G query heads. The 8 waves
+// of a workgroup take two roles, one of each per SIMD: waves 0..3 consume
+// (32 query rows each: scores, softmax, P V on the matrix cores), waves 4..3+4
+// produce (each loads one 16-key cache block of the next tile and rebuilds its
+// keys on the vector units), so the rebuild of tile t+1 overlaps the matrix
+// work on tile t. All tiles of one KV head are dealt to one XCD, so the keys
+// they share (the common prefix) stream through one L2.
 //
 // Matrix-core mapping (16x16 tiles):
 //   X^T[dim, key]   = B_k^T L_k^T        (per wave: its 16-key block, 16x16x16 / 16x16x32)
@@ -25,15 +29,12 @@
 //   C^T[rank, row] += L_v^T P^T
 //   O^T            += B_v^T C^T          (after the loop; C split into bf16 hi + lo)
 //
-// Software pipeline (one barrier per tile): while the matrix cores work on
-// the scores of tile t and on P V of tile t-1, the vector units rebuild the
-// keys of tile t+1 into the other key buffer and the loads of tile t+2 are
-// in flight; then the softmax of tile t runs. Keys are double-buffered in
-// LDS, V^T and L_v^T triple-buffered (tile t-1 is still read while t+1 is
-// written). The rotation of the adapter key at position 64t + o is split by
-// angle addition into a per-tile part (64t, one table of 64 pairs per tile)
-// and a per-lane part (o, fixed for the whole loop), so no transcendental is
-// evaluated per element.
+// Pipeline (one barrier per tile): while the consumers work on tile t, the
+// producers rebuild tile t+1 into the other LDS buffers (keys, V^T, L_v^T
+// double-buffered) and the loads of tile t+2 are in flight. The rotation of
+// the adapter key at position 64t + o is split by angle addition into a
+// per-tile part (64t, one table of 64 pairs per tile) and a per-lane part (o,
+// fixed for the whole loop), so no transcendental is evaluated per element.
 #include <type_traits>
 
 #include "device_common.h"
@@ -48,7 +49,8 @@ constexpr int kTile = 64;      // keys per tile (4 cache blocks)
 constexpr int kKPitch = D + 8;          // LDS row pitch of the key tile (bf16)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
 constexpr int kKBufs = 2;
-constexpr int kVBufs = 3;
+constexpr int kVBufs = 2;
+constexpr int kThreads = 512;  // 4 consumer + 4 producer waves
 constexpr float kMaxSlack = 8.f;  // log2 of the largest probability kept before a rescale
 
 // (cos, sin) of one angle given in revolutions, with the revolution count
@@ -67,7 +69,7 @@ struct TileRegs {  // this wave's cache block of one tile, on its way from HBM
 };
 
 template <int RP>
-__global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) {
+__global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NRT = RP / 16;
   constexpr int KC = RP >= 32 ? RP / 32 : 1;
   __shared__ __align__(16) uint16_t s_k[kKBufs][kTile * kKPitch];   // rebuilt keys [key][dim]
@@ -108,11 +110,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
+  const bool producer = wave >= 4;  // waves 4..7: block `pw` of every tile
+  const int pw = wave & 3;
   const int lc = lane & 15;
   const int lg = lane >> 4;
 
   // ---- preamble: B_k^T, B_v^T, rotary tables ----
-  for (int e = tid; e < RP * (D / 8); e += 256) {
+  for (int e = tid; e < RP * (D / 8); e += kThreads) {
     const int k = e % RP, d8 = (e / RP) * 8;
     uint4 vk = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
     if (k < r) {
@@ -139,21 +143,167 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
   };
   rot_table(0);
   rot_table(1);
-  // per-lane part: key offset 16 wave + lc within the tile, pairs 16cb + 4lg + jj
-  float co[4][4], so[4][4];
-  {
-    const double off = (double)(kBlock * wave + lc);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float2 cs = cos_sin_rev(off * s_rev[16 * cb + 4 * lg + jj]);
-        co[cb][jj] = cs.x;
-        so[cb][jj] = cs.y;
+  const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
+  const int n_tiles = (kv_end + kTile - 1) / kTile;
+  const float csc = a.sm_scale_log2;
+
+  __syncthreads();  // B_k^T, B_v^T and the first rotary tables are in LDS
+
+  if (producer) {
+    // per-lane part (producers): key offset 16 pw + lc within the tile, pairs 16cb + 4lg + jj
+    float co[4][4], so[4][4];
+    {
+      const double off = (double)(kBlock * pw + lc);
+  #pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const float2 cs = cos_sin_rev(off * s_rev[16 * cb + 4 * lg + jj]);
+          co[cb][jj] = cs.x;
+          so[cb][jj] = cs.y;
+        }
+    }
+
+    // ---- global -> registers: block `pw` of tile t. Blocks past the
+    // visible keys get zero-length buffer ranges, so their loads return 0. ----
+    TileRegs<RP> tr;
+    auto load_tile = [&](int t) __attribute__((always_inline)) {
+      const int key0 = t * kTile + kBlock * pw;
+      const bool valid = key0 < kv_end;
+      const int phys = uniform(bt_row[valid ? key0 / kBlock : 0]);
+      const int on = valid ? 1 : 0;
+      const auto rk = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
+                               on * kBlock * D * 2);
+  #pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        tr.kbl[cb] = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
+        tr.kbh[cb] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
       }
+      const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, on * kBlock * r * 2);
+      if constexpr (RP == 16) {
+        const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
+        tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
+      } else {
+  #pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          tr.lk[kc] = bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
+      }
+      const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
+                               on * D * kBlock * 2);
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) tr.vv[u] = bld16(rv, ((2 * lane + (u >> 1)) * kBlock + 8 * (u & 1)) * 2);
+      const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, on * r * kBlock * 2);
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = lane + 64 * u, rank = e >> 1;
+        tr.lvv[u] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
+      }
+    };
+
+    // ---- registers -> LDS: V^T, L_v^T as loaded; keys rebuilt as
+    // K_base + rope(B_k^T L_k^T), rounded once to bf16. LAST marks the final
+    // tile, the only one that can hold positions >= T (zeroed in V and L_v,
+    // whose products with P = 0 must stay finite). ----
+    auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
+      constexpr bool LAST = decltype(last_tag)::value;
+      const int key0 = t * kTile + kBlock * pw;
+      uint16_t* sk = s_k[t & 1];
+      uint16_t* sv = s_v[t % kVBufs];
+      uint16_t* slv = s_lv[t % kVBufs];
+  #pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        uint4 v = tr.vv[u];
+        if constexpr (LAST) {
+          const int kk = key0 + 8 * (u & 1);
+          uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
+  #pragma unroll
+          for (int p = 0; p < 4; ++p)
+            w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
+        }
+        *reinterpret_cast<uint4*>(sv + (2 * lane + (u >> 1)) * kVPitch + kBlock * pw + 8 * (u & 1)) = v;
+      }
+  #pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = lane + 64 * u;
+        if (e < 2 * RP) {
+          uint4 v = tr.lvv[u];
+          if constexpr (LAST) {
+            const int kk = key0 + 8 * (e & 1);
+            uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
+  #pragma unroll
+            for (int p = 0; p < 4; ++p)
+              w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
+          }
+          *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
+        }
+      }
+      const float* rot = s_rot[t & 1];
+  #pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (RP == 16) {
+          const uint2 al_ = *reinterpret_cast<const uint2*>(s_bt + (16 * cb + lc) * RP + 4 * lg);
+          const uint2 ah_ = *reinterpret_cast<const uint2*>(s_bt + (16 * (cb + 4) + lc) * RP + 4 * lg);
+          const uint2 lk2 = make_uint2(tr.lk[0].x, tr.lk[0].y);
+          xl = mfma16(as_i16x4(al_), as_i16x4(lk2), xl);
+          xh = mfma16(as_i16x4(ah_), as_i16x4(lk2), xh);
+        } else {
+  #pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            const uint4 al_ = *reinterpret_cast<const uint4*>(s_bt + (16 * cb + lc) * RP + 32 * kc + 8 * lg);
+            const uint4 ah_ = *reinterpret_cast<const uint4*>(s_bt + (16 * (cb + 4) + lc) * RP + 32 * kc + 8 * lg);
+            xl = mfma32(as_bf16x8(al_), as_bf16x8(tr.lk[kc]), xl);
+            xh = mfma32(as_bf16x8(ah_), as_bf16x8(tr.lk[kc]), xh);
+          }
+        }
+        const float4 r01 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg));
+        const float4 r23 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg) + 4);
+        const float cB[4] = {r01.x, r01.z, r23.x, r23.z};
+        const float sB[4] = {r01.y, r01.w, r23.y, r23.w};
+        const float kl[4] = {__uint_as_float(tr.kbl[cb].x << 16), __uint_as_float(tr.kbl[cb].x & 0xFFFF0000u),
+                             __uint_as_float(tr.kbl[cb].y << 16), __uint_as_float(tr.kbl[cb].y & 0xFFFF0000u)};
+        const float kh[4] = {__uint_as_float(tr.kbh[cb].x << 16), __uint_as_float(tr.kbh[cb].x & 0xFFFF0000u),
+                             __uint_as_float(tr.kbh[cb].y << 16), __uint_as_float(tr.kbh[cb].y & 0xFFFF0000u)};
+        float y1[4], y2[4];
+  #pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          // angle of pair 16cb + 4lg + jj at position 64t + 16 pw + lc
+          const float c = cB[jj] * co[cb][jj] - sB[jj] * so[cb][jj];
+          const float sn = sB[jj] * co[cb][jj] + cB[jj] * so[cb][jj];
+          const float u = xl[jj], w = xh[jj];
+          y1[jj] = __builtin_fmaf(-w, sn, __builtin_fmaf(u, c, kl[jj]));
+          y2[jj] = __builtin_fmaf(u, sn, __builtin_fmaf(w, c, kh[jj]));
+        }
+        *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) =
+            pack_bf16x4(y1[0], y1[1], y1[2], y1[3]);
+        *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) =
+            pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
+      }
+    };
+
+
+    load_tile(0);
+    if (n_tiles == 1)
+      store_tile(0, std::true_type{});
+    else
+      store_tile(0, std::false_type{});
+    if (n_tiles > 1) load_tile(1);
+    __syncthreads();  // tile 0 is in LDS
+    for (int kt = 0; kt < n_tiles; ++kt) {
+      if (kt + 2 < n_tiles) {
+        store_tile(kt + 1, std::false_type{});
+        load_tile(kt + 2);
+        rot_table(kt + 2);
+      } else if (kt + 1 < n_tiles) {
+        store_tile(kt + 1, std::true_type{});
+      }
+      __syncthreads();  // tile kt is consumed and tile kt + 1 is in LDS
+    }
+    return;
   }
 
-  // ---- query operands: this wave's rows 32w + 16rt + lc ----
+  // ---- consumers ----
+  // ---- query operands (consumers): this wave's rows 32w + 16rt + lc ----
   bf16x8 qb[2][4];
   int rpos[2];    // position of the row's query token
   bool rok[2];
@@ -161,7 +311,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
   for (int rt = 0; rt < 2; ++rt) {
     const int row = 32 * wave + 16 * rt + lc;
     const int t = row / G, j = row % G;
-    rok[rt] = (row < TQ * G) && (t < n_tok);
+    rok[rt] = !producer && (row < TQ * G) && (t < n_tok);
     rpos[rt] = p0 + t;
     const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(q0 + t0 + t) * a.Hq + h * G + j) * D;
 #pragma unroll
@@ -181,127 +331,6 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
 #pragma unroll
     for (int i = 0; i < NRT; ++i) cacc[rt][i] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
-  const int n_tiles = (kv_end + kTile - 1) / kTile;
-  const float csc = a.sm_scale_log2;
-
-  // ---- global -> registers: block `wave` of tile t. Blocks past the
-  // visible keys get zero-length buffer ranges, so their loads return 0. ----
-  TileRegs<RP> tr;
-  auto load_tile = [&](int t) __attribute__((always_inline)) {
-    const int key0 = t * kTile + kBlock * wave;
-    const bool valid = key0 < kv_end;
-    const int phys = uniform(bt_row[valid ? key0 / kBlock : 0]);
-    const int on = valid ? 1 : 0;
-    const auto rk = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
-                             on * kBlock * D * 2);
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      tr.kbl[cb] = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
-      tr.kbh[cb] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
-    }
-    const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, on * kBlock * r * 2);
-    if constexpr (RP == 16) {
-      const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
-      tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
-    } else {
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        tr.lk[kc] = bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
-    }
-    const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
-                             on * D * kBlock * 2);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) tr.vv[u] = bld16(rv, ((2 * lane + (u >> 1)) * kBlock + 8 * (u & 1)) * 2);
-    const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, on * r * kBlock * 2);
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = lane + 64 * u, rank = e >> 1;
-      tr.lvv[u] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
-    }
-  };
-
-  // ---- registers -> LDS: V^T, L_v^T as loaded; keys rebuilt as
-  // K_base + rope(B_k^T L_k^T), rounded once to bf16. LAST marks the final
-  // tile, the only one that can hold positions >= T (zeroed in V and L_v,
-  // whose products with P = 0 must stay finite). ----
-  auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
-    constexpr bool LAST = decltype(last_tag)::value;
-    const int key0 = t * kTile + kBlock * wave;
-    uint16_t* sk = s_k[t & 1];
-    uint16_t* sv = s_v[t % kVBufs];
-    uint16_t* slv = s_lv[t % kVBufs];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint4 v = tr.vv[u];
-      if constexpr (LAST) {
-        const int kk = key0 + 8 * (u & 1);
-        uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
-      }
-      *reinterpret_cast<uint4*>(sv + (2 * lane + (u >> 1)) * kVPitch + kBlock * wave + 8 * (u & 1)) = v;
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int e = lane + 64 * u;
-      if (e < 2 * RP) {
-        uint4 v = tr.lvv[u];
-        if constexpr (LAST) {
-          const int kk = key0 + 8 * (e & 1);
-          uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
-        }
-        *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * wave + 8 * (e & 1)) = v;
-      }
-    }
-    const float* rot = s_rot[t & 1];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-      f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
-      if constexpr (RP == 16) {
-        const uint2 al_ = *reinterpret_cast<const uint2*>(s_bt + (16 * cb + lc) * RP + 4 * lg);
-        const uint2 ah_ = *reinterpret_cast<const uint2*>(s_bt + (16 * (cb + 4) + lc) * RP + 4 * lg);
-        const uint2 lk2 = make_uint2(tr.lk[0].x, tr.lk[0].y);
-        xl = mfma16(as_i16x4(al_), as_i16x4(lk2), xl);
-        xh = mfma16(as_i16x4(ah_), as_i16x4(lk2), xh);
-      } else {
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          const uint4 al_ = *reinterpret_cast<const uint4*>(s_bt + (16 * cb + lc) * RP + 32 * kc + 8 * lg);
-          const uint4 ah_ = *reinterpret_cast<const uint4*>(s_bt + (16 * (cb + 4) + lc) * RP + 32 * kc + 8 * lg);
-          xl = mfma32(as_bf16x8(al_), as_bf16x8(tr.lk[kc]), xl);
-          xh = mfma32(as_bf16x8(ah_), as_bf16x8(tr.lk[kc]), xh);
-        }
-      }
-      const float4 r01 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg));
-      const float4 r23 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg) + 4);
-      const float cB[4] = {r01.x, r01.z, r23.x, r23.z};
-      const float sB[4] = {r01.y, r01.w, r23.y, r23.w};
-      const float kl[4] = {__uint_as_float(tr.kbl[cb].x << 16), __uint_as_float(tr.kbl[cb].x & 0xFFFF0000u),
-                           __uint_as_float(tr.kbl[cb].y << 16), __uint_as_float(tr.kbl[cb].y & 0xFFFF0000u)};
-      const float kh[4] = {__uint_as_float(tr.kbh[cb].x << 16), __uint_as_float(tr.kbh[cb].x & 0xFFFF0000u),
-                           __uint_as_float(tr.kbh[cb].y << 16), __uint_as_float(tr.kbh[cb].y & 0xFFFF0000u)};
-      float y1[4], y2[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        // angle of pair 16cb + 4lg + jj at position 64t + 16 wave + lc
-        const float c = cB[jj] * co[cb][jj] - sB[jj] * so[cb][jj];
-        const float sn = sB[jj] * co[cb][jj] + cB[jj] * so[cb][jj];
-        const float u = xl[jj], w = xh[jj];
-        y1[jj] = __builtin_fmaf(-w, sn, __builtin_fmaf(u, c, kl[jj]));
-        y2[jj] = __builtin_fmaf(u, sn, __builtin_fmaf(w, c, kh[jj]));
-      }
-      *reinterpret_cast<uint2*>(sk + (kBlock * wave + lc) * kKPitch + 16 * cb + 4 * lg) =
-          pack_bf16x4(y1[0], y1[1], y1[2], y1[3]);
-      *reinterpret_cast<uint2*>(sk + (kBlock * wave + lc) * kKPitch + 64 + 16 * cb + 4 * lg) =
-          pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
-    }
-  };
-
   // ---- S^T[key, row] for the tile's 4 key blocks x this wave's 2 row tiles ----
   f32x4 sacc[4][2];
   auto scores = [&](int t) __attribute__((always_inline)) {
@@ -413,44 +442,13 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
       softmax(t, std::false_type{});
   };
 
-  // ---- pipeline ----
-  __syncthreads();  // B_k^T, B_v^T and the first rotary tables are in LDS
-  load_tile(0);
-  if (n_tiles == 1)
-    store_tile(0, std::true_type{});
-  else
-    store_tile(0, std::false_type{});
-  if (n_tiles > 1) load_tile(1);
-  __syncthreads();
-  // tile 0
-  scores(0);
-  if (n_tiles > 2) {
-    store_tile(1, std::false_type{});
-    load_tile(2);
-    rot_table(2);
-  } else if (n_tiles == 2) {
-    store_tile(1, std::true_type{});
-  }
-  softmax_tile(0);
-  __syncthreads();
-  int kt = 1;
-  for (; kt + 2 < n_tiles; ++kt) {  // steady state
+  __syncthreads();  // tile 0 is in LDS
+  for (int kt = 0; kt < n_tiles; ++kt) {
     scores(kt);
-    pv(kt - 1);
-    store_tile(kt + 1, std::false_type{});
-    load_tile(kt + 2);
-    rot_table(kt + 2);
     softmax_tile(kt);
-    __syncthreads();
+    pv(kt);
+    __syncthreads();  // tile kt is consumed and tile kt + 1 is in LDS
   }
-  for (; kt < n_tiles; ++kt) {  // the last one or two tiles
-    scores(kt);
-    pv(kt - 1);
-    if (kt + 1 < n_tiles) store_tile(kt + 1, std::true_type{});
-    softmax_tile(kt);
-    __syncthreads();
-  }
-  pv(n_tiles - 1);
 
   // ---- epilogue: O^T += B_v^T C^T (C as bf16 hi + lo), divide by l, store ----
 #pragma unroll
@@ -491,7 +489,7 @@ __global__ __launch_bounds__(256) void prefill_bf16_kernel(const PrefillArgs a) 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const int n_work = a.Hkv * a.S * a.q_tiles;
   const int per = (n_work + kNumXcd - 1) / kNumXcd;
-  const dim3 grid(per * kNumXcd), block(256);
+  const dim3 grid(per * kNumXcd), block(kThreads);
   switch (a.rp) {
     case 16: hipLaunchKernelGGL(prefill_bf16_kernel<16>, grid, block, 0, stream, a); break;
     case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, block, 0, stream, a); break;
