@@ -30,8 +30,11 @@
 //   O^T            += B_v^T C^T          (after the loop; C split into bf16 hi + lo)
 //
 // Pipeline (one barrier per tile): while the consumers work on tile t, the
-// producers rebuild tile t+1 into the other LDS buffers (keys, V^T, L_v^T
-// double-buffered) and the loads of tile t+2 are in flight. The rotation of
+// producers rebuild tile t+1 into the other LDS buffers and the loads of tile
+// t+2 are in flight. Each consumer issues the scores of tile t and P V of tile
+// t-1 together and runs the softmax of tile t while the matrix cores work
+// through them; so keys are double-buffered in LDS and V^T, L_v^T
+// triple-buffered (tile t-1 is read while t+1 is written). The rotation of
 // the adapter key at position 64t + o is split by angle addition into a
 // per-tile part (64t, one table of 64 pairs per tile) and a per-lane part (o,
 // fixed for the whole loop), so no transcendental is evaluated per element.
@@ -49,7 +52,7 @@ constexpr int kTile = 64;      // keys per tile (4 cache blocks)
 constexpr int kKPitch = D + 8;          // LDS row pitch of the key tile (bf16)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
 constexpr int kKBufs = 2;
-constexpr int kVBufs = 2;
+constexpr int kVBufs = 3;
 constexpr int kThreads = 512;  // 4 consumer + 4 producer waves
 constexpr float kMaxSlack = 8.f;  // log2 of the largest probability kept before a rescale
 
@@ -443,12 +446,16 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   };
 
   __syncthreads();  // tile 0 is in LDS
-  for (int kt = 0; kt < n_tiles; ++kt) {
+  scores(0);
+  softmax_tile(0);
+  __syncthreads();  // scores of tile 0 are done and tile 1 is in LDS
+  for (int kt = 1; kt < n_tiles; ++kt) {
     scores(kt);
+    pv(kt - 1);
     softmax_tile(kt);
-    pv(kt);
-    __syncthreads();  // tile kt is consumed and tile kt + 1 is in LDS
+    __syncthreads();  // keys of tile kt and values of tile kt - 1 are consumed; tile kt + 1 is in LDS
   }
+  pv(n_tiles - 1);
 
   // ---- epilogue: O^T += B_v^T C^T (C as bf16 hi + lo), divide by l, store ----
 #pragma unroll
