@@ -28,7 +28,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
 * ``B`` is [r, Hkv*d] with column ``h*d + i``; one L row serves every KV head;
 * a decode query sits at position T-1 and sees keys 0..T-1; prefill query i of
   a chunk of q_len new tokens sits at T - q_len + i and sees keys 0..position;
-* softmax scale is an explicit argument (1/sqrt(d) unless stated).
+* softmax scale is an explicit argument (1/sqrt(d) unless stated);
+* a projection without an adapter (B = None) keeps its base cache unchanged,
+  and a sequence without an agent has neither adapter.
 
 Everything is evaluated in float64 with materialised full-dimension K and V
 and a plain two-pass softmax: this file is the definition, not a fast path.
@@ -75,12 +77,20 @@ def materialise_kv(kb, vb, lk, lv, bk, bv, theta: float):
 
     kb, vb [T, Hkv, d] base rows; lk, lv [T, r] low-rank rows; bk, bv [r, Hkv*d].
     K[n] = kb[n] + rope_n(lk[n] bk),  V[n] = vb[n] + lv[n] bv.
+
+    A projection without an adapter passes None for its B (and L): its cache
+    is the base part alone. PReCache, appendix Table 13 caption, compares
+    against adapters on the query and value projections only (no key
+    adapter), and its Figure 1 caption batches adapter-free paths (no adapter
+    at all) with adapted ones.
     """
     T, Hkv, d = kb.shape
-    k_ad = adapter_term(lk, bk, Hkv, d)
-    v_ad = adapter_term(lv, bv, Hkv, d)
-    K = np.asarray(kb, np.float64) + rope_rotate(k_ad, np.arange(T), theta)
-    V = np.asarray(vb, np.float64) + v_ad
+    K = np.array(kb, dtype=np.float64)
+    V = np.array(vb, dtype=np.float64)
+    if bk is not None:
+        K = K + rope_rotate(adapter_term(lk, bk, Hkv, d), np.arange(T), theta)
+    if bv is not None:
+        V = V + adapter_term(lv, bv, Hkv, d)
     return K, V
 
 

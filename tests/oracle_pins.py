@@ -119,6 +119,30 @@ def pin_adapter_matches_sdpa_on_built_cache(o):
     assert np.allclose(got, ref, atol=1e-12, rtol=0), np.abs(got - ref).max()
 
 
+def pin_absent_adapters_sdpa(o):
+    """A projection without an adapter (B None) keeps its base cache: with no
+    adapter at all the result is SDPA over (kb, vb); with only a value adapter
+    it is SDPA over (kb, vb + lv bv), unaffected by the rotary base (rotary
+    acts on the key adapter alone); with only a key adapter and rotary off it
+    is SDPA over (kb + lk bk, vb)."""
+    rng = np.random.default_rng(10)
+    for nq in (1, 4):
+        c = _rand_case(rng, T=12, Hq=6, Hkv=3, d=4, r=2, nq=nq)
+        T, Hkv, d = c["kb"].shape
+        pos = np.arange(T - nq, T)
+        K_ad = c["kb"] + (c["lk"] @ c["bk"]).reshape(T, Hkv, d)
+        V_ad = c["vb"] + (c["lv"] @ c["bv"]).reshape(T, Hkv, d)
+        cases = (
+            (dict(c, lk=None, lv=None, bk=None, bv=None), 5e5, c["kb"], c["vb"]),
+            (dict(c, lk=None, bk=None), 5e5, c["kb"], V_ad),
+            (dict(c, lv=None, bv=None), 0.0, K_ad, c["vb"]),
+        )
+        for args, theta, K, V in cases:
+            got = o.lora_attention(**args, sm_scale=0.45, theta=theta)
+            ref = _sdpa(c["q"], K, V, pos, 0.45)
+            assert np.allclose(got, ref, atol=1e-12, rtol=0), (nq, theta, np.abs(got - ref).max())
+
+
 def pin_uniform_scores_mean(o):
     """q = 0 gives equal weights: out = mean_n V[n] = mean(vb) + mean(lv) bv."""
     rng = np.random.default_rng(4)

@@ -64,6 +64,23 @@ def _rope_on_v_too(kb, vb, lk, lv, bk, bv, theta):
     return K, vb + O.rope_rotate(v_ad, np.arange(T), theta)
 
 
+def _absent_key_drops_value(kb, vb, lk, lv, bk, bv, theta):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+    return K, (np.asarray(vb, np.float64).copy() if bk is None else V)
+
+
+def _absent_key_rotates_base(kb, vb, lk, lv, bk, bv, theta):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+    if bk is None:
+        K = O.rope_rotate(np.asarray(kb, np.float64), np.arange(kb.shape[0]), theta)
+    return K, V
+
+
+def _absent_value_drops_key(kb, vb, lk, lv, bk, bv, theta):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+    return (np.asarray(kb, np.float64).copy() if bv is None else K), V
+
+
 def _gqa_modulo(j, Hq, Hkv):
     return j % Hkv
 
@@ -89,6 +106,9 @@ MUTATIONS = {
     "drop_value_adapter": ("materialise_kv", _drop_v_adapter),
     "drop_key_adapter": ("materialise_kv", _drop_k_adapter),
     "rotate_value_adapter": ("materialise_kv", _rope_on_v_too),
+    "absent_key_adapter_drops_value_adapter": ("materialise_kv", _absent_key_drops_value),
+    "absent_key_adapter_rotates_base_keys": ("materialise_kv", _absent_key_rotates_base),
+    "absent_value_adapter_drops_key_adapter": ("materialise_kv", _absent_value_drops_key),
     "gqa_modulo_mapping": ("kv_head_of", _gqa_modulo),
     "causal_off_by_one": ("attend", _causal_exclusive),
     "missing_softmax_scale": ("attend", _no_scale),

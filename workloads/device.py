@@ -32,16 +32,16 @@ class DeviceWorkload:
     block_tables: torch.Tensor
     context_lens: torch.Tensor
     group_offsets: torch.Tensor
-    agent_ids: torch.Tensor
+    agent_ids: torch.Tensor  # None without any adapter
     lk_pools: list
     lv_pools: list
     bk: list
     bv: list
-    lk_ptrs: torch.Tensor
+    lk_ptrs: torch.Tensor  # pointer tables: None for a projection without an adapter
     lv_ptrs: torch.Tensor
     bk_ptrs: torch.Tensor
     bv_ptrs: torch.Tensor
-    ranks: torch.Tensor
+    ranks: torch.Tensor  # None without any adapter
     cu_q_lens: torch.Tensor
     max_context_len: int
     max_q_len: int
@@ -72,13 +72,18 @@ def upload(w: Workload, device="cuda", poison: bool = False, host_pools=None) ->
     lk_of_agent = [lk_pools[w.pool_of_agent[a]] for a in range(w.n_agents)]
     lv_of_agent = [lv_pools[w.pool_of_agent[a]] for a in range(w.n_agents)]
     ctx = [w.context_len(s) for s in range(w.S)]
+    adapted = w.has_k or w.has_v
+    # a projection without an adapter passes NULL pointer tables; with no
+    # adapter at all the agent ids and ranks are not passed either
     return DeviceWorkload(
         w=w, q=q, k_base=k_base, v_base=v_base,
         block_tables=i32(w.block_tables()), context_lens=i32(ctx),
         group_offsets=i32(w.group_offsets) if w.group_offsets is not None else None,
-        agent_ids=i32([sq.agent for sq in w.seqs]),
+        agent_ids=i32([sq.agent for sq in w.seqs]) if adapted else None,
         lk_pools=lk_pools, lv_pools=lv_pools, bk=bk, bv=bv,
-        lk_ptrs=ptrs(lk_of_agent), lv_ptrs=ptrs(lv_of_agent), bk_ptrs=ptrs(bk), bv_ptrs=ptrs(bv),
-        ranks=i32(w.ranks), cu_q_lens=i32(w.q_offsets()),
-        max_context_len=max(ctx), max_q_len=max(sq.q_len for sq in w.seqs), max_rank=max(w.ranks),
+        lk_ptrs=ptrs(lk_of_agent) if w.has_k else None, lv_ptrs=ptrs(lv_of_agent) if w.has_v else None,
+        bk_ptrs=ptrs(bk) if w.has_k else None, bv_ptrs=ptrs(bv) if w.has_v else None,
+        ranks=i32(w.ranks) if adapted else None, cu_q_lens=i32(w.q_offsets()),
+        max_context_len=max(ctx), max_q_len=max(sq.q_len for sq in w.seqs),
+        max_rank=max(w.ranks) if adapted else 0,
     )

@@ -116,6 +116,10 @@ class Workload:
     spare_blocks: int = 0  # unused physical blocks (poison targets)
     prefill: bool = False
     sm_scale: float = None
+    # projections that carry an adapter: "kv" (both), "v" (value only: no key
+    # adapter), "k" (key only) or "none". A sequence whose agent is -1 has no
+    # adapter in any case. Draws do not depend on this field.
+    adapt: str = "kv"
     _cache: dict = field(default_factory=dict, repr=False)
 
     # ------------------------------------------------------------------ draws
@@ -190,19 +194,34 @@ class Workload:
     def q_offsets(self) -> np.ndarray:
         return np.concatenate([[0], np.cumsum([sq.q_len for sq in self.seqs])]).astype(np.int32)
 
+    @property
+    def has_k(self) -> bool:
+        return "k" in self.adapt
+
+    @property
+    def has_v(self) -> bool:
+        return "v" in self.adapt
+
     def logical(self, s: int) -> dict:
-        """Unpaged float64 arrays of sequence s, as the oracle consumes them."""
+        """Unpaged float64 arrays of sequence s, as the oracle consumes them
+        (None for the low-rank rows and B of a projection without an adapter)."""
         sq = self.seqs[s]
-        pool = self.pool_of_agent[sq.agent]
         parts = [self.segment_data(i) for i in sq.segments]
         kb = np.concatenate([p[0] for p in parts]).astype(np.float64)
         vb = np.concatenate([p[1] for p in parts]).astype(np.float64)
-        lk = np.concatenate([p[2][pool] for p in parts]).astype(np.float64)
-        lv = np.concatenate([p[3][pool] for p in parts]).astype(np.float64)
-        bk, bv = self.adapter(sq.agent)
         qo = self.q_offsets()
         q = self.q_all()[qo[s] : qo[s + 1]].astype(np.float64)
-        return dict(q=q, kb=kb, vb=vb, lk=lk, lv=lv, bk=bk.astype(np.float64), bv=bv.astype(np.float64))
+        out = dict(q=q, kb=kb, vb=vb, lk=None, lv=None, bk=None, bv=None)
+        if sq.agent >= 0:
+            pool = self.pool_of_agent[sq.agent]
+            bk, bv = self.adapter(sq.agent)
+            if self.has_k:
+                out["lk"] = np.concatenate([p[2][pool] for p in parts]).astype(np.float64)
+                out["bk"] = bk.astype(np.float64)
+            if self.has_v:
+                out["lv"] = np.concatenate([p[3][pool] for p in parts]).astype(np.float64)
+                out["bv"] = bv.astype(np.float64)
+        return out
 
     # ----------------------------------------------------------------- layout
     def block_tables(self) -> np.ndarray:
@@ -296,12 +315,13 @@ def decode_workload(
     shuffle=True,
     spare_blocks=0,
     seed=0,
+    adapt="kv",
 ):
     """Decode batch: groups of sequences; each group shares one base context.
 
     ``shared_l`` gives every agent one low-rank pool (shared-A adapters);
     otherwise each agent has its own pool. Sequence i of the flattened groups
-    belongs to agent ``agent_of_seq[i]`` (default: i).
+    belongs to agent ``agent_of_seq[i]`` (default: i; -1: no adapter).
     """
     S = sum(group_sizes)
     agent_of_seq = list(agent_of_seq) if agent_of_seq is not None else list(range(S))
@@ -314,7 +334,7 @@ def decode_workload(
     segments, seqs, go = [], [], [0]
     s = 0
     for g, (gs, T) in enumerate(zip(group_sizes, context_lens)):
-        pools = sorted({pool_of_agent[agent_of_seq[s + i]] for i in range(gs)})
+        pools = sorted({pool_of_agent[agent_of_seq[s + i]] for i in range(gs) if agent_of_seq[s + i] >= 0})
         segments.append(Segment(T=T, pools=tuple(pools)))
         for i in range(gs):
             seqs.append(SeqSpec(segments=(g,), agent=agent_of_seq[s + i]))
@@ -323,7 +343,7 @@ def decode_workload(
     return Workload(
         name=name, dtype=dtype, Hq=Hq, Hkv=Hkv, d=d, theta=theta, ranks=list(ranks),
         pool_of_agent=pool_of_agent, pool_rank=pool_rank, segments=segments, seqs=seqs,
-        group_offsets=go, seed=seed, shuffle=shuffle, spare_blocks=spare_blocks,
+        group_offsets=go, seed=seed, shuffle=shuffle, spare_blocks=spare_blocks, adapt=adapt,
     )
 
 
@@ -359,11 +379,16 @@ def prefill_workload(
     shuffle=True,
     spare_blocks=0,
     seed=0,
+    adapt="kv",
+    agents=None,
 ):
     """Prefill chunks: each agent appends ``q_lens[a]`` new tokens after one
     shared prefix; one shared-A low-rank pool; agent a's new rows live in its
-    own blocks. Query i of agent a sits at position prefix + i."""
+    own blocks. Query i of agent a sits at position prefix + i. ``agents``
+    gives the agent of each chunk (default: chunk a is agent a; -1: no
+    adapter)."""
     A = len(q_lens)
+    agents = list(range(A)) if agents is None else list(agents)
     segments = []
     if prefix:
         assert prefix % BLOCK == 0
@@ -371,11 +396,12 @@ def prefill_workload(
     base = len(segments)
     for a in range(A):
         segments.append(Segment(T=q_lens[a], pools=(0,)))
-    seqs = [SeqSpec(segments=((0,) if prefix else ()) + (base + a,), agent=a, q_len=q_lens[a]) for a in range(A)]
+    seqs = [SeqSpec(segments=((0,) if prefix else ()) + (base + a,), agent=agents[a], q_len=q_lens[a])
+            for a in range(A)]
     return Workload(
         name=name, dtype=dtype, Hq=Hq, Hkv=Hkv, d=d, theta=theta, ranks=[rank] * A,
         pool_of_agent=[0] * A, pool_rank=[rank], segments=segments, seqs=seqs,
-        seed=seed, shuffle=shuffle, spare_blocks=spare_blocks, prefill=True,
+        seed=seed, shuffle=shuffle, spare_blocks=spare_blocks, prefill=True, adapt=adapt,
     )
 
 
