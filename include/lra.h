@@ -118,16 +118,27 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
  *                 shared base component of LRAgent's abstract). At most
  *                 16 / (Hq/Hkv) sequences of a group share one pass; larger
  *                 groups are served in several passes.
- *   agent_ids     int32 [S], in [0, N_agents).
+ *   agent_ids     int32 [S], in [0, N_agents), or -1 for a sequence without
+ *                 an adapter (it attends over the base cache alone; PReCache
+ *                 Figure 1 caption batches such adapter-free paths with
+ *                 adapted ones).
  *   l_k_pools, l_v_pools
  *                 device arrays [N_agents] of device pointers to each agent's
  *                 low-rank pools ([NB,16,r_a] and [NB,r_a,16]). Agents with
  *                 shared-A adapters pass the same pointers (LRAgent abstract:
  *                 shared-A lets the low-rank cache itself be shared).
  *   b_k, b_v      device arrays [N_agents] of device pointers to [r_a, Hkv*d].
+ *                 b_k == NULL: the call has no key adapter (K = K_base; adapters
+ *                 on q and v only, the setting PReCache's appendix Table 13
+ *                 caption compares against); l_k_pools is then not read and
+ *                 may be NULL, and no key is rebuilt. b_v == NULL likewise
+ *                 for values (V = V_base, l_v_pools not read). Both NULL:
+ *                 plain attention over the base cache; agent_ids, ranks and
+ *                 N_agents are not read and max_rank must be 0.
  *   ranks         int32 [N_agents], each in 1..max_rank; with LRA_BF16 each
  *                 rank must be a multiple of 8 (rows are read 16 bytes at a time).
- *   max_rank      (host) 1..64. d: 64 or 128 (bf16: 128). block_size: 16.
+ *   max_rank      (host) 1..64, or 0 without adapters (pass the same value to
+ *                 the workspace query). d: 64 or 128 (bf16: 128). block_size: 16.
  *   sm_scale      softmax scale (usually 1/sqrt(d)).
  *   rope_theta    rotary base for the adapter key term; 0 disables it.
  *   dtype         LRA_BF16 (split-K kernel on MFMA, fp32 accumulate) or
@@ -167,7 +178,10 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
  *
  *   q, out        [cu_q_lens[S], Hq, d]; cu_q_lens int32 [S+1], q_len_s <= T_s.
  *   max_q_len     (host) >= every q_len_s.
- *   Everything else as for decode (no grouping). dtype: LRA_BF16, d = 128.
+ *   Everything else as for decode (no grouping; agent id -1 and NULL b_k /
+ *   b_v as there: without a key adapter the key tiles are the base keys as
+ *   stored, without a value adapter no rank-space accumulator is kept).
+ *   dtype: LRA_BF16, d = 128.
  *   workspace     lora_attn_prefill_workspace_size(...) bytes (may be 0,
  *                 then workspace may be NULL).
  * ---------------------------------------------------------------------- */

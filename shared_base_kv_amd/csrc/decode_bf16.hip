@@ -128,30 +128,34 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, Wo
 // Main kernel: one workgroup of kDecodeWaves waves per (group, row tile,
 // split, KV head). NA is a compile-time bound on the agents of a row tile
 // (a tile with fewer runs with zero B_k / L rows for the missing ones).
+// KAD / VAD: the call has key / value adapters; without one, that part of
+// the work (its low-rank loads, staging and products) is not compiled in.
 // Writes the split's record (m, l, seq, nact, O' per row), or the finished
 // rows when the context fits one split.
-template <int RP, int NA>
+template <int RP, int NA, bool KAD, bool VAD>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const DecodeArgs a) {
   constexpr int NRT = RP / 16;
   constexpr int KC = RP >= 32 ? RP / 32 : 1;
-  constexpr int PW = D + RP;  // floats per row of a merged state (O then C)
+  constexpr int PW = D + (VAD ? RP : 0);  // floats per row of a merged state (O, then C)
   constexpr int NT = kDecodeWaves * 64;
   constexpr int HW = kDecodeWaves / 2;
-  constexpr int kBtBytes = NA * D * RP * 2;
+  constexpr int kBtBytes = KAD ? NA * D * RP * 2 : 0;
   constexpr int kMergeBytes = HW * 16 * PW * 4;
   constexpr int kRegion = kBtBytes > kMergeBytes ? kBtBytes : kMergeBytes;
   static_assert(NA * RP <= 256, "staged B_k^T / B_v^T of a tile exceed their LDS budget");
+  constexpr bool ADAPT = KAD || VAD;
 
   __shared__ __align__(16) unsigned char s_region[kRegion];  // B_k^T [al][dim][k] in the loop, merge buffer after
-  __shared__ __align__(16) uint16_t s_bvt[NA * D * RP];      // B_v^T [al][dim][k]
-  __shared__ __align__(16) uint16_t s_q[16 * kQPitch];       // query tile [row][dim]
-  __shared__ __align__(16) uint16_t s_qp[16 * kQpPitch];     // f16 query tile, k slots of the adapter product
-  __shared__ __align__(16) f16x2 s_roff[16 * kRotPitch];     // (cos, sin) of lc theta_i, [lc][i]
-  __shared__ __align__(16) f16x2 s_rbase[kDecodeWaves][kMaxRopePairs];  // per wave: (cos, sin) of tb theta_i
+  __shared__ __align__(16) uint16_t s_bvt[VAD ? NA * D * RP : 8];          // B_v^T [al][dim][k]
+  __shared__ __align__(16) uint16_t s_q[16 * kQPitch];                     // query tile [row][dim]
+  __shared__ __align__(16) uint16_t s_qp[KAD ? 16 * kQpPitch : 8];         // f16 query tile, k slots of the adapter product
+  __shared__ __align__(16) f16x2 s_roff[KAD ? 16 * kRotPitch : 4];         // (cos, sin) of lc theta_i, [lc][i]
+  __shared__ __align__(16) f16x2 s_rbase[KAD ? kDecodeWaves : 1][kMaxRopePairs];  // per wave: (cos, sin) of tb theta_i
   __shared__ double s_rev[kMaxRopePairs];
   __shared__ TileAgent s_agent[NA];
   __shared__ float s_ml[2][HW][16];
   __shared__ int s_shared_l;
+  __shared__ int s_lead;  // first agent slot of the tile with an adapter (its rows travel with the blocks)
 
   // ---- work item; consecutive logical items are dealt to one XCD ----
   const int per = (a.n_work + kNumXcd - 1) / kNumXcd;
@@ -194,18 +198,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
                      __attribute__((always_inline)) {
     const bool ok = bi < nb;
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
-    const auto rlk = buf_rsrc(lk0 + (size_t)phys * kBlock * r0, ok ? kBlock * r0 * 2 : 0);
-    if constexpr (RP == 16) {
-      B.lk16 = bld8(rlk, (4 * lg < r0) ? (lc * r0 + 4 * lg) * 2 : kOob);
-    } else {
+    if constexpr (KAD) {
+      const auto rlk = buf_rsrc(lk0 + (size_t)phys * kBlock * r0, ok ? kBlock * r0 * 2 : 0);
+      if constexpr (RP == 16) {
+        B.lk16 = bld8(rlk, (4 * lg < r0) ? (lc * r0 + 4 * lg) * 2 : kOob);
+      } else {
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-        B.lk32[kc] = as_bf16x8(bld16(rlk, (32 * kc + 8 * lg < r0) ? (lc * r0 + 32 * kc + 8 * lg) * 2 : kOob));
+        for (int kc = 0; kc < KC; ++kc)
+          B.lk32[kc] = as_bf16x8(bld16(rlk, (32 * kc + 8 * lg < r0) ? (lc * r0 + 32 * kc + 8 * lg) * 2 : kOob));
+      }
     }
-    const auto rlv = buf_rsrc(lv0 + (size_t)phys * r0 * kBlock, ok ? r0 * kBlock * 2 : 0);
+    if constexpr (VAD) {
+      const auto rlv = buf_rsrc(lv0 + (size_t)phys * r0 * kBlock, ok ? r0 * kBlock * 2 : 0);
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr)
-      B.lv[rr] = bld8(rlv, (16 * rr + lc < r0) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+      for (int rr = 0; rr < NRT; ++rr)
+        B.lv[rr] = bld8(rlv, (16 * rr + lc < r0) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
+    }
     const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
                              ok ? D * kBlock * 2 : 0);
 #pragma unroll
@@ -215,16 +223,20 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // ---- (1) the rotary table (kernel arguments), then the base keys of this
   // wave's first block; later waits for the table cover nothing else ----
   double rev_arg = 0.0;
-  if (tid < kMaxRopePairs) rev_arg = a.rope_rev[tid];
+  if (KAD && tid < kMaxRopePairs) rev_arg = a.rope_rev[tid];
   __builtin_amdgcn_sched_barrier(0);
   Blk<RP> bufA, bufB;
   load_k(bufA, wave);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- (2) agent table, from scalar loads only (which do not wait behind
-  // the vector loads in flight) ----
-  if (wave == 0) {
-    int sh = 1;
+  // the vector loads in flight). A sequence without an agent (id -1) gets
+  // rank 0 and no pointers: its B rows stage as zero, so whatever low-rank
+  // rows its slot is given contribute nothing. The lead is the first slot
+  // with an adapter; its low-rank rows travel with the blocks, and the
+  // tile's pools count as shared when every adapted slot reads the lead's. ----
+  if (ADAPT && wave == 0) {
+    int sh = 1, lead = -1;
     const uint16_t *lk0 = nullptr, *lv0 = nullptr;
     int r0 = 0;
     for (int al = 0; al < NA; ++al) {
@@ -232,30 +244,40 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       if (al < ns) {
         const int seq = s0 + al;
         const int ag = sload(a.agent_ids + seq);
-        t.lk = (const uint16_t*)sload(a.lk + ag);
-        t.lv = (const uint16_t*)sload(a.lv + ag);
-        t.bk = (const uint16_t*)sload(a.bk + ag);
-        t.bv = (const uint16_t*)sload(a.bv + ag);
-        t.r = sload(a.ranks + ag);
         t.seq = seq;
-        if (al == 0) {
-          lk0 = t.lk;
-          lv0 = t.lv;
-          r0 = t.r;
-        } else {
-          sh &= (t.lk == lk0) & (t.lv == lv0) & (t.r == r0);
+        if (ag >= 0) {
+          if constexpr (KAD) {
+            t.lk = (const uint16_t*)sload(a.lk + ag);
+            t.bk = (const uint16_t*)sload(a.bk + ag);
+          }
+          if constexpr (VAD) {
+            t.lv = (const uint16_t*)sload(a.lv + ag);
+            t.bv = (const uint16_t*)sload(a.bv + ag);
+          }
+          t.r = sload(a.ranks + ag);
+          if (lead < 0) {
+            lead = al;
+            lk0 = t.lk;
+            lv0 = t.lv;
+            r0 = t.r;
+          } else {
+            sh &= (t.lk == lk0) & (t.lv == lv0) & (t.r == r0);
+          }
         }
       }
       if (lane == 0) s_agent[al] = t;
     }
-    if (lane == 0) s_shared_l = sh;
+    if (lane == 0) {
+      s_shared_l = sh;
+      s_lead = lead < 0 ? 0 : lead;
+    }
   }
-  if (tid < kMaxRopePairs) s_rev[tid] = rev_arg;
+  if (KAD && tid < kMaxRopePairs) s_rev[tid] = rev_arg;
   __syncthreads();
 
   // ---- (3) staging loads: B_k, B_v rows of head h per agent, the query tile ----
-  constexpr int kItemsB = NA * RP * (D / 8);  // 8-dim chunks of B_k (and of B_v)
-  constexpr int kPerB = (kItemsB + NT - 1) / NT;
+  constexpr int kItemsB = ADAPT ? NA * RP * (D / 8) : 0;  // 8-dim chunks of B_k (and of B_v)
+  constexpr int kPerB = ADAPT ? (kItemsB + NT - 1) / NT : 1;
   uint4 stk[kPerB], stv[kPerB];
 #pragma unroll
   for (int i = 0; i < kPerB; ++i) {
@@ -264,8 +286,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     stk[i] = make_uint4(0, 0, 0, 0);
     stv[i] = make_uint4(0, 0, 0, 0);
     if (e < kItemsB && k < s_agent[al].r) {
-      stk[i] = ld16(s_agent[al].bk + (size_t)k * HD + h * D + d8);
-      stv[i] = ld16(s_agent[al].bv + (size_t)k * HD + h * D + d8);
+      if constexpr (KAD) stk[i] = ld16(s_agent[al].bk + (size_t)k * HD + h * D + d8);
+      if constexpr (VAD) stv[i] = ld16(s_agent[al].bv + (size_t)k * HD + h * D + d8);
     }
   }
   uint4 stq = make_uint4(0, 0, 0, 0);
@@ -274,9 +296,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     stq = ld16((const uint16_t*)a.q + ((size_t)(s0 + qrow / G) * a.Hq + h * G + (qrow % G)) * D + qd8);
 
   // ---- (4) the rest of the first block ----
-  const uint16_t* lk0 = uniform_ptr(s_agent[0].lk);
-  const uint16_t* lv0 = uniform_ptr(s_agent[0].lv);
-  const int r0 = uniform(s_agent[0].r);
+  const int lead = ADAPT ? uniform(s_lead) : 0;
+  const uint16_t* lk0 = ADAPT ? uniform_ptr(s_agent[lead].lk) : nullptr;
+  const uint16_t* lv0 = ADAPT ? uniform_ptr(s_agent[lead].lv) : nullptr;
+  const int r0 = ADAPT ? uniform(s_agent[lead].r) : 0;
   load_lv(bufA, wave, lk0, lv0, r0);
 
   // ---- (5) staged values into LDS (waits for the first keys and the
@@ -291,28 +314,32 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       const uint16_t* pv = reinterpret_cast<const uint16_t*>(&stv[i]);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        s_bt[((size_t)al * D + d8 + j) * RP + k] = pk[j];
-        s_bvt[((size_t)al * D + d8 + j) * RP + k] = pv[j];
+        if constexpr (KAD) s_bt[((size_t)al * D + d8 + j) * RP + k] = pk[j];
+        if constexpr (VAD) s_bvt[((size_t)al * D + d8 + j) * RP + k] = pv[j];
       }
     }
   }
   if (tid < 16 * (D / 8)) {
     *reinterpret_cast<uint4*>(s_q + qrow * kQPitch + qd8) = stq;
-    // f16 copy in the k-slot order of the adapter product: for dim tile cb
-    // and k-group g, slots 2j and 2j + 1 hold dims 16cb + 4g + j and + 64
-    const uint16_t* pq = reinterpret_cast<const uint16_t*>(&stq);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int d = qd8 + j, dd = d & 63;
-      const int slot = (dd >> 4) * 32 + ((dd >> 2) & 3) * 8 + 2 * (dd & 3) + (d >> 6);
-      s_qp[qrow * kQpPitch + slot] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(pq[j]));
-    }
   }
-  // per-column rotation table: entries (lc, i) for lc < 16, i < 64
-  for (int e = tid; e < 16 * kMaxRopePairs; e += NT) {
-    const int col = e / kMaxRopePairs, i = e % kMaxRopePairs;
-    const float2 cs = cos_sin_rev((double)col * s_rev[i]);
-    s_roff[col * kRotPitch + i] = f16x2{(_Float16)cs.x, (_Float16)cs.y};
+  if constexpr (KAD) {
+    if (tid < 16 * (D / 8)) {
+      // f16 copy in the k-slot order of the adapter product: for dim tile cb
+      // and k-group g, slots 2j and 2j + 1 hold dims 16cb + 4g + j and + 64
+      const uint16_t* pq = reinterpret_cast<const uint16_t*>(&stq);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int d = qd8 + j, dd = d & 63;
+        const int slot = (dd >> 4) * 32 + ((dd >> 2) & 3) * 8 + 2 * (dd & 3) + (d >> 6);
+        s_qp[qrow * kQpPitch + slot] = __builtin_bit_cast(uint16_t, (_Float16)bf16_to_f32(pq[j]));
+      }
+    }
+    // per-column rotation table: entries (lc, i) for lc < 16, i < 64
+    for (int e = tid; e < 16 * kMaxRopePairs; e += NT) {
+      const int col = e / kMaxRopePairs, i = e % kMaxRopePairs;
+      const float2 cs = cos_sin_rev((double)col * s_rev[i]);
+      s_roff[col * kRotPitch + i] = f16x2{(_Float16)cs.x, (_Float16)cs.y};
+    }
   }
   __syncthreads();
 
@@ -321,7 +348,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const bool row_ok = row_al < ns && lc < a.apt * G;
   const uint16_t* qrow_p = s_q + lc * kQPitch;
   const uint16_t* qp_row = s_qp + lc * kQpPitch;
-  const double rev_lane = s_rev[lane];
+  const double rev_lane = KAD ? s_rev[lane] : 0.0;
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 o[8];
@@ -338,9 +365,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   int ag_r[NA];
 #pragma unroll
   for (int al = 0; al < NA; ++al) {
-    ag_lk[al] = uniform_ptr(s_agent[al].lk);
-    ag_lv[al] = uniform_ptr(s_agent[al].lv);
-    ag_r[al] = uniform(s_agent[al].r);
+    ag_lk[al] = ADAPT ? uniform_ptr(s_agent[al].lk) : nullptr;
+    ag_lv[al] = ADAPT ? uniform_ptr(s_agent[al].lv) : nullptr;
+    ag_r[al] = ADAPT ? uniform(s_agent[al].r) : 0;
   }
   // per-agent low-rank rows of block bi (zero-length ranges past the split):
   // key rows (K) and value rows (V) separately
@@ -351,7 +378,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 #pragma unroll
     for (int al = 1; al < NA; ++al) {
       const int ra = ag_r[al];
-      if (keys) {
+      if (KAD && keys) {
         const auto rl = buf_rsrc(ag_lk[al] + (size_t)phys * kBlock * ra, ok ? kBlock * ra * 2 : 0);
         if constexpr (RP == 16) {
           ar.lk16[al - 1] = bld8(rl, (4 * lg < ra) ? (lc * ra + 4 * lg) * 2 : kOob);
@@ -362,7 +389,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
                 as_bf16x8(bld16(rl, (32 * kc + 8 * lg < ra) ? (lc * ra + 32 * kc + 8 * lg) * 2 : kOob));
         }
       }
-      if (vals) {
+      if (VAD && vals) {
         const auto rv = buf_rsrc(ag_lv[al] + (size_t)phys * ra * kBlock, ok ? ra * kBlock * 2 : 0);
 #pragma unroll
         for (int rr = 0; rr < NRT; ++rr)
@@ -373,7 +400,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 
   // Other agents' rows are loaded one block ahead when they fit in 16
   // registers; larger ones are loaded at the start of the block's compute.
-  constexpr bool kAgentAhead = (NA - 1) * (RP / 4) <= 16;
+  constexpr int kAgentRegs = (KAD ? RP / 8 : 0) + (VAD ? RP / 8 : 0);  // per agent and block
+  constexpr bool kAgentAhead = (NA - 1) * kAgentRegs <= 16;
   auto compute = [&](const Blk<RP>& B, const AgentRows<RP, NA>& ar_ahead, int bi) __attribute__((always_inline)) {
     AgentRows<RP, NA> ar_here;
     if constexpr (!kAgentAhead) load_agents(ar_here, bi, true, false);
@@ -465,16 +493,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
         }
       }
     };
-    if (shared_l) {
-      if (a.rope)
-        adapter(std::true_type{}, std::true_type{});
-      else
-        adapter(std::false_type{}, std::true_type{});
-    } else {
-      if (a.rope)
-        adapter(std::true_type{}, std::false_type{});
-      else
-        adapter(std::false_type{}, std::false_type{});
+    if constexpr (KAD) {
+      if (shared_l) {
+        if (a.rope)
+          adapter(std::true_type{}, std::true_type{});
+        else
+          adapter(std::false_type{}, std::true_type{});
+      } else {
+        if (a.rope)
+          adapter(std::true_type{}, std::false_type{});
+        else
+          adapter(std::false_type{}, std::false_type{});
+      }
     }
     if constexpr (!kAgentAhead) load_agents(ar_here, bi, false, true);
     f32x4 sad = sa[0];
@@ -486,7 +516,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     float mx = -INFINITY;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      sv[jj] = tv[jj] ? (sb[jj] + sad[jj]) * a.sm_scale_log2 : -INFINITY;
+      sv[jj] = tv[jj] ? (KAD ? sb[jj] + sad[jj] : sb[jj]) * a.sm_scale_log2 : -INFINITY;
       mx = fmaxf(mx, sv[jj]);
     }
     mx = wave_max_across_groups(mx);
@@ -510,8 +540,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) o[i] *= alpha;
+      if constexpr (VAD) {
 #pragma unroll
-      for (int i = 0; i < NRT; ++i) acl[i] *= alpha;
+        for (int i = 0; i < NRT; ++i) acl[i] *= alpha;
+      }
     }
     // P^T operand: k slots 0..3 = tokens 4lg + jj
     const uint2 pop = pack_bf16x4(p[0], p[1], p[2], p[3]);
@@ -520,18 +552,20 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     for (int cb = 0; cb < 8; ++cb)
       o[cb] = mfma16(as_i16x4(make_uint2(B.vr[cb].x & m01, B.vr[cb].y & m23)), as_i16x4(pop), o[cb]);
     // C^T += L_v^T P^T (per agent pool; rows of other agents masked out)
-    if (shared_l) {
+    if constexpr (VAD) {
+      if (shared_l) {
 #pragma unroll
-      for (int rr = 0; rr < NRT; ++rr)
-        acl[rr] = mfma16(as_i16x4(make_uint2(B.lv[rr].x & m01, B.lv[rr].y & m23)), as_i16x4(pop), acl[rr]);
-    } else {
+        for (int rr = 0; rr < NRT; ++rr)
+          acl[rr] = mfma16(as_i16x4(make_uint2(B.lv[rr].x & m01, B.lv[rr].y & m23)), as_i16x4(pop), acl[rr]);
+      } else {
 #pragma unroll
-      for (int al = 0; al < NA; ++al) {
-        const uint2 pm = (row_ok && row_al == al) ? pop : make_uint2(0, 0);
+        for (int al = 0; al < NA; ++al) {
+          const uint2 pm = (row_ok && row_al == al) ? pop : make_uint2(0, 0);
 #pragma unroll
-        for (int rr = 0; rr < NRT; ++rr) {
-          const uint2 lvr = al == 0 ? B.lv[rr] : ar.lv[al > 0 ? al - 1 : 0][rr];
-          acl[rr] = mfma16(as_i16x4(make_uint2(lvr.x & m01, lvr.y & m23)), as_i16x4(pm), acl[rr]);
+          for (int rr = 0; rr < NRT; ++rr) {
+            const uint2 lvr = al == 0 ? B.lv[rr] : ar.lv[al > 0 ? al - 1 : 0][rr];
+            acl[rr] = mfma16(as_i16x4(make_uint2(lvr.x & m01, lvr.y & m23)), as_i16x4(pm), acl[rr]);
+          }
         }
       }
     }
@@ -571,8 +605,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     float* ob = obuf + ((size_t)slot * 16 + lc) * PW;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) *reinterpret_cast<f32x4*>(ob + 16 * cb + 4 * lg) = o[cb];
+    if constexpr (VAD) {
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) *reinterpret_cast<f32x4*>(ob + D + 16 * rr + 4 * lg) = acl[rr];
+      for (int rr = 0; rr < NRT; ++rr) *reinterpret_cast<f32x4*>(ob + D + 16 * rr + 4 * lg) = acl[rr];
+    }
   }
   __syncthreads();
   if (wave < HW) {
@@ -586,10 +622,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       const f32x4 v = *reinterpret_cast<const f32x4*>(ob + 16 * cb + 4 * lg);
       *reinterpret_cast<f32x4*>(ob + 16 * cb + 4 * lg) = w1 * o[cb] + w2 * v;
     }
+    if constexpr (VAD) {
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(ob + D + 16 * rr + 4 * lg);
-      *reinterpret_cast<f32x4*>(ob + D + 16 * rr + 4 * lg) = w1 * acl[rr] + w2 * v;
+      for (int rr = 0; rr < NRT; ++rr) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(ob + D + 16 * rr + 4 * lg);
+        *reinterpret_cast<f32x4*>(ob + D + 16 * rr + 4 * lg) = w1 * acl[rr] + w2 * v;
+      }
     }
     if (lg == 0) {
       s_ml[0][wave][lc] = mm;
@@ -614,7 +652,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // merged rank-space accumulator C of this lane's row, as bf16 hi + lo, per rank tile
   uint2 chi[NRT], clo[NRT];
 #pragma unroll
-  for (int rr = 0; rr < NRT; ++rr) {
+  for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
     f32x4 cm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < HW; ++j)
@@ -629,7 +667,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     clo[rr] = pack_bf16x4(lo[0], lo[1], lo[2], lo[3]);
   }
   const bool used = lc < ns * G;
-  const int seq = s_agent[row_al < NA ? row_al : 0].seq;
+  const int seq = s0 + row_al;
   float* part = a.partials + (((size_t)wi.tile_id * a.nsplit + c) * 16 + lc) * a.part_stride;
 #pragma unroll
   for (int dt = 0; dt < DTW; ++dt) {
@@ -639,7 +677,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     for (int j = 0; j < HW; ++j)
       acc += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + 16 * cbt + 4 * lg);
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) {
+    for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
 #pragma unroll
       for (int al = 0; al < NA; ++al) {
         const bool mine = row_ok && row_al == al;
@@ -737,9 +775,28 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
   }
 }
 
-template <int RP, int NA>
+template <int RP, int NA, bool KAD, bool VAD>
 void launch_main(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_bf16_kernel<RP, NA>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+}
+
+template <bool KAD, bool VAD>
+bool launch_variant(const DecodeArgs& a, int rp, int na, dim3 grid, hipStream_t stream) {
+  switch (rp * 100 + na) {
+    case 1601: launch_main<16, 1, KAD, VAD>(a, grid, stream); return true;
+    case 1602: launch_main<16, 2, KAD, VAD>(a, grid, stream); return true;
+    case 1604: launch_main<16, 4, KAD, VAD>(a, grid, stream); return true;
+    case 1608: launch_main<16, 8, KAD, VAD>(a, grid, stream); return true;
+    case 1616: launch_main<16, 16, KAD, VAD>(a, grid, stream); return true;
+    case 3201: launch_main<32, 1, KAD, VAD>(a, grid, stream); return true;
+    case 3202: launch_main<32, 2, KAD, VAD>(a, grid, stream); return true;
+    case 3204: launch_main<32, 4, KAD, VAD>(a, grid, stream); return true;
+    case 3208: launch_main<32, 8, KAD, VAD>(a, grid, stream); return true;
+    case 6401: launch_main<64, 1, KAD, VAD>(a, grid, stream); return true;
+    case 6402: launch_main<64, 2, KAD, VAD>(a, grid, stream); return true;
+    case 6404: launch_main<64, 4, KAD, VAD>(a, grid, stream); return true;
+    default: return false;
+  }
 }
 
 }  // namespace
@@ -748,21 +805,19 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t s
   const int per = (a.n_work + kNumXcd - 1) / kNumXcd;
   const dim3 grid(per * kNumXcd);
   const int n_rows = a.num_groups * a.row_tiles * a.Hkv * 16;
-  switch (rp * 100 + na) {
-    case 1601: launch_main<16, 1>(a, grid, stream); break;
-    case 1602: launch_main<16, 2>(a, grid, stream); break;
-    case 1604: launch_main<16, 4>(a, grid, stream); break;
-    case 1608: launch_main<16, 8>(a, grid, stream); break;
-    case 1616: launch_main<16, 16>(a, grid, stream); break;
-    case 3201: launch_main<32, 1>(a, grid, stream); break;
-    case 3202: launch_main<32, 2>(a, grid, stream); break;
-    case 3204: launch_main<32, 4>(a, grid, stream); break;
-    case 3208: launch_main<32, 8>(a, grid, stream); break;
-    case 6401: launch_main<64, 1>(a, grid, stream); break;
-    case 6402: launch_main<64, 2>(a, grid, stream); break;
-    case 6404: launch_main<64, 4>(a, grid, stream); break;
-    default: return hipErrorInvalidValue;
+  const bool kad = a.bk != nullptr, vad = a.bv != nullptr;
+  bool launched;
+  if (kad && vad)
+    launched = launch_variant<true, true>(a, rp, na, grid, stream);
+  else if (vad)
+    launched = launch_variant<false, true>(a, rp, na, grid, stream);
+  else if (kad)
+    launched = launch_variant<true, false>(a, rp, na, grid, stream);
+  else {  // no adapter: one variant serves every tile width (no per-agent state)
+    launch_main<16, 1, false, false>(a, grid, stream);
+    launched = true;
   }
+  if (!launched) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit <= 1) return e;
   hipLaunchKernelGGL(decode_bf16_combine, dim3(n_rows), dim3(64), 0, stream, a);

@@ -7,7 +7,9 @@
 // to device memory; the value adapter is accumulated in rank space,
 // C = sum_n p_n L_v[n], and applied once at the end as C B_v.
 // One workgroup per (sequence, KV head); the G query heads of that KV head
-// share every chunk. Online softmax in the base-2 domain.
+// share every chunk. Online softmax in the base-2 domain. A call without
+// key (value) adapters, or a sequence without an agent, takes rank 0 for
+// that part: its loops run zero times and its pools are not read.
 #include "device_common.h"
 #include "internal.h"
 
@@ -43,12 +45,15 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = a.G;
   const int HD = a.Hkv * D;
-  const int ag = a.agent_ids[s];
-  const int r = a.ranks[ag];
-  const float* lk = (const float*)a.lk[ag];
-  const float* lv = (const float*)a.lv[ag];
-  const float* bk = (const float*)a.bk[ag];
-  const float* bv = (const float*)a.bv[ag];
+  const bool kad = a.bk != nullptr, vad = a.bv != nullptr;
+  const int ag = (kad || vad) ? a.agent_ids[s] : -1;
+  const int r_ag = ag >= 0 ? a.ranks[ag] : 0;
+  const int rk = kad ? r_ag : 0;  // rank of the key adapter (0: none)
+  const int rv = vad ? r_ag : 0;  // rank of the value adapter (0: none)
+  const float* lk = rk ? (const float*)a.lk[ag] : nullptr;
+  const float* lv = rv ? (const float*)a.lv[ag] : nullptr;
+  const float* bk = rk ? (const float*)a.bk[ag] : nullptr;
+  const float* bv = rv ? (const float*)a.bv[ag] : nullptr;
   const float* kb = (const float*)a.kb;
   const float* vb = (const float*)a.vb;
   const int T = a.context_lens[s];
@@ -81,14 +86,13 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
       float k1 = 0.f, k2 = 0.f;
       if (n < T) {
         const int phys = sPhys[t / kBlock], slot = n % kBlock;
-        const float* lrow = lk + ((size_t)phys * kBlock + slot) * r;
         float x1 = 0.f, x2 = 0.f;
-        for (int k = 0; k < r; ++k) {
-          const float l = lrow[k];
+        for (int k = 0; k < rk; ++k) {
+          const float l = lk[((size_t)phys * kBlock + slot) * rk + k];
           x1 = fmaf(l, bk[(size_t)k * HD + h * D + i], x1);
           x2 = fmaf(l, bk[(size_t)k * HD + h * D + i + HALF], x2);
         }
-        if (a.rope) {
+        if (a.rope && rk) {
           const double x = (double)n * sRev[i];
           const float f = (float)(x - __builtin_floor(x));
           const float c = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
@@ -148,11 +152,11 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     for (int u = 0; u < 4; ++u) {
       const int e = tid + 256 * u;
       const int row = e / 64, k = e % 64;
-      if (row < G && k < r) {
+      if (row < G && k < rv) {
         float v = accC[u] * sAlpha[row];
         for (int t = 0; t < kChunk && n0 + t < T; ++t) {
           const int phys = sPhys[t / kBlock];
-          v = fmaf(sP[row][t], lv[((size_t)phys * r + k) * kBlock + t % kBlock], v);
+          v = fmaf(sP[row][t], lv[((size_t)phys * rv + k) * kBlock + t % kBlock], v);
         }
         accC[u] = v;
       }
@@ -171,7 +175,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
     const int row = e / D, i = e % D;
     if (row < G) {
       float v = acc[u];
-      for (int k = 0; k < r; ++k) v = fmaf(sC[row][k], bv[(size_t)k * HD + h * D + i], v);
+      for (int k = 0; k < rv; ++k) v = fmaf(sC[row][k], bv[(size_t)k * HD + h * D + i], v);
       ((float*)a.out)[((size_t)s * a.Hq + h * G + row) * D + i] = v / sL[row];
     }
   }

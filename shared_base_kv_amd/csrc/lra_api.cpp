@@ -33,6 +33,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 size_t round_up(size_t a, size_t b) { return (a + b - 1) / b * b; }
 
+// max_rank 0 (a call without adapters) plans as rank 16.
 int pad_rank(int max_rank) { return max_rank <= 16 ? 16 : (max_rank <= 32 ? 32 : 64); }
 
 // Launch plan of the decode kernels; depends on host sizes only.
@@ -79,13 +80,31 @@ int check_decode_sizes(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
   if (dtype != LRA_F32 && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "dtype %d is not LRA_F32 or LRA_BF16", dtype);
   if (dtype == LRA_BF16 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "bf16 kernels are built for d = 128 (got %d)", d);
   if (dtype == LRA_F32 && d != 64 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "fp32 kernel supports d = 64 or 128 (got %d)", d);
-  if (max_rank < 1 || max_rank > 64) return fail(LRA_ERR_UNSUPPORTED, "max_rank must be in 1..64 (got %d)", max_rank);
+  if (max_rank < 0 || max_rank > 64)
+    return fail(LRA_ERR_UNSUPPORTED, "max_rank must be in 1..64, or 0 without adapters (got %d)", max_rank);
   if (max_ctx < 1) return fail(LRA_ERR_INVALID_ARG, "max_context_len must be >= 1 (got %d)", max_ctx);
   if (dtype == LRA_BF16 && max_ctx > kMaxSplits * kMaxSplitBlocks * kBlock)
     return fail(LRA_ERR_UNSUPPORTED, "bf16 decode supports contexts up to %d tokens (got %d)",
                 kMaxSplits * kMaxSplitBlocks * kBlock, max_ctx);
   if (S > 0 && (num_groups < 1 || num_groups > S))
     return fail(LRA_ERR_INVALID_ARG, "num_groups must be in 1..S (got %d, S=%d)", num_groups, S);
+  return LRA_OK;
+}
+
+// Adapter arguments: b_k (b_v) NULL means the call has no key (value)
+// adapter and its low-rank pool table is not read; with neither, agent ids,
+// ranks and N_agents are not read either and max_rank must be 0.
+int check_adapters(const int32_t* agent_ids, const void* const* l_k_pools, const void* const* l_v_pools,
+                   const void* const* b_k, const void* const* b_v, const int32_t* ranks, int max_rank, int N_agents) {
+  if (!b_k && !b_v) {
+    if (max_rank != 0) return fail(LRA_ERR_INVALID_ARG, "max_rank must be 0 when b_k and b_v are both NULL (got %d)", max_rank);
+    return LRA_OK;
+  }
+  if (max_rank < 1) return fail(LRA_ERR_INVALID_ARG, "max_rank must be in 1..64 with an adapter (got %d)", max_rank);
+  if (N_agents < 1) return fail(LRA_ERR_INVALID_ARG, "N_agents must be >= 1 (got %d)", N_agents);
+  if (!agent_ids || !ranks) return fail(LRA_ERR_INVALID_ARG, "agent_ids and ranks must be non-null with an adapter");
+  if (b_k && !l_k_pools) return fail(LRA_ERR_INVALID_ARG, "l_k_pools must be non-null when b_k is given");
+  if (b_v && !l_v_pools) return fail(LRA_ERR_INVALID_ARG, "l_v_pools must be non-null when b_v is given");
   return LRA_OK;
 }
 
@@ -183,12 +202,12 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   if (rc != LRA_OK) return rc;
   if (S == 0) return ok();
   if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
-  if (N_agents < 1) return fail(LRA_ERR_INVALID_ARG, "N_agents must be >= 1 (got %d)", N_agents);
   if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
     return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
-  if (!q || !k_base || !v_base || !block_tables || !context_lens || !agent_ids || !l_k_pools || !l_v_pools || !b_k ||
-      !b_v || !ranks || !out)
+  if (!q || !k_base || !v_base || !block_tables || !context_lens || !out)
     return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+  rc = check_adapters(agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, N_agents);
+  if (rc != LRA_OK) return rc;
   if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
     return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
   if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
@@ -255,14 +274,14 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
   if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "prefill supports LRA_BF16 only");
   if (S == 0) return ok();
   if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
-  if (N_agents < 1) return fail(LRA_ERR_INVALID_ARG, "N_agents must be >= 1 (got %d)", N_agents);
   if (max_q_len < 1 || max_q_len > max_context_len)
     return fail(LRA_ERR_INVALID_ARG, "max_q_len must be in 1..max_context_len (got %d)", max_q_len);
   if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
     return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
-  if (!q || !k_base || !v_base || !block_tables || !context_lens || !cu_q_lens || !agent_ids || !l_k_pools ||
-      !l_v_pools || !b_k || !b_v || !ranks || !out)
+  if (!q || !k_base || !v_base || !block_tables || !context_lens || !cu_q_lens || !out)
     return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+  rc = check_adapters(agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, N_agents);
+  if (rc != LRA_OK) return rc;
   if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
     return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
   if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)

@@ -71,16 +71,20 @@ struct TileRegs {  // this wave's cache block of one tile, on its way from HBM
   uint4 lvv[2];          // L_v^T items lane, lane + 64: rank item/2, keys 8 (item%2) .. +7
 };
 
-template <int RP>
+// KAD / VAD: the call has key / value adapters; without one, that part of
+// the work (low-rank loads, staging, rebuild or rank-space products) is not
+// compiled in. A sequence without an agent (id -1) runs with rank 0: its
+// low-rank loads read nothing and its staged B rows are zero.
+template <int RP, bool KAD, bool VAD>
 __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArgs a) {
   constexpr int NRT = RP / 16;
   constexpr int KC = RP >= 32 ? RP / 32 : 1;
-  __shared__ __align__(16) uint16_t s_k[kKBufs][kTile * kKPitch];   // rebuilt keys [key][dim]
-  __shared__ __align__(16) uint16_t s_v[kVBufs][D * kVPitch];       // V^T [dim][key]
-  __shared__ __align__(16) uint16_t s_lv[kVBufs][RP * kVPitch];     // L_v^T [rank][key]
-  __shared__ __align__(16) uint16_t s_bt[D * RP];                   // B_k^T [dim][rank]
-  __shared__ __align__(16) uint16_t s_bvt[D * RP];                  // B_v^T [dim][rank]
-  __shared__ __align__(16) float s_rot[kKBufs][2 * kMaxRopePairs];  // (cos, sin) of 64 t theta_i
+  __shared__ __align__(16) uint16_t s_k[kKBufs][kTile * kKPitch];           // rebuilt keys [key][dim]
+  __shared__ __align__(16) uint16_t s_v[kVBufs][D * kVPitch];               // V^T [dim][key]
+  __shared__ __align__(16) uint16_t s_lv[kVBufs][VAD ? RP * kVPitch : 8];   // L_v^T [rank][key]
+  __shared__ __align__(16) uint16_t s_bt[KAD ? D * RP : 8];                 // B_k^T [dim][rank]
+  __shared__ __align__(16) uint16_t s_bvt[VAD ? D * RP : 8];                // B_v^T [dim][rank]
+  __shared__ __align__(16) float s_rot[kKBufs][2 * kMaxRopePairs];          // (cos, sin) of 64 t theta_i
   __shared__ double s_rev[kMaxRopePairs];
 
   const int G = a.G;
@@ -101,12 +105,12 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   const int T = a.context_lens[s];
   const int p0 = T - q_len + t0;        // position of the tile's first query
   const int kv_end = p0 + n_tok;        // keys 0..kv_end-1 are visible to some row
-  const int ag = a.agent_ids[s];
-  const uint16_t* lk = (const uint16_t*)a.lk[ag];
-  const uint16_t* lv = (const uint16_t*)a.lv[ag];
-  const uint16_t* bk = (const uint16_t*)a.bk[ag];
-  const uint16_t* bv = (const uint16_t*)a.bv[ag];
-  const int r = a.ranks[ag];
+  const int ag = (KAD || VAD) ? a.agent_ids[s] : -1;
+  const uint16_t* lk = (KAD && ag >= 0) ? (const uint16_t*)a.lk[ag] : nullptr;
+  const uint16_t* lv = (VAD && ag >= 0) ? (const uint16_t*)a.lv[ag] : nullptr;
+  const uint16_t* bk = (KAD && ag >= 0) ? (const uint16_t*)a.bk[ag] : nullptr;
+  const uint16_t* bv = (VAD && ag >= 0) ? (const uint16_t*)a.bv[ag] : nullptr;
+  const int r = ag >= 0 ? a.ranks[ag] : 0;
   const int HD = a.Hkv * D;
   const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
 
@@ -119,30 +123,32 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   const int lg = lane >> 4;
 
   // ---- preamble: B_k^T, B_v^T, rotary tables ----
-  for (int e = tid; e < RP * (D / 8); e += kThreads) {
+  for (int e = tid; (KAD || VAD) && e < RP * (D / 8); e += kThreads) {
     const int k = e % RP, d8 = (e / RP) * 8;
     uint4 vk = make_uint4(0, 0, 0, 0), vw = make_uint4(0, 0, 0, 0);
     if (k < r) {
-      vk = ld16(bk + (size_t)k * HD + h * D + d8);
-      vw = ld16(bv + (size_t)k * HD + h * D + d8);
+      if constexpr (KAD) vk = ld16(bk + (size_t)k * HD + h * D + d8);
+      if constexpr (VAD) vw = ld16(bv + (size_t)k * HD + h * D + d8);
     }
     const uint16_t* pk = reinterpret_cast<const uint16_t*>(&vk);
     const uint16_t* pv = reinterpret_cast<const uint16_t*>(&vw);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      s_bt[(d8 + i) * RP + k] = pk[i];
-      s_bvt[(d8 + i) * RP + k] = pv[i];
+      if constexpr (KAD) s_bt[(d8 + i) * RP + k] = pk[i];
+      if constexpr (VAD) s_bvt[(d8 + i) * RP + k] = pv[i];
     }
   }
   // rotary revolutions per position, staged through LDS (a lane-indexed read
   // of the kernel-argument array would go through scratch)
-  if (tid < kMaxRopePairs) s_rev[tid] = a.rope_rev[tid];
+  if (KAD && tid < kMaxRopePairs) s_rev[tid] = a.rope_rev[tid];
   __syncthreads();
   // per-tile table: every wave computes pair `lane` and writes the same value
-  const double rev_lane = s_rev[lane];
+  const double rev_lane = KAD ? s_rev[lane] : 0.0;
   auto rot_table = [&](int t) __attribute__((always_inline)) {
-    const float2 cs = cos_sin_rev((double)(t * kTile) * rev_lane);
-    *reinterpret_cast<float2*>(&s_rot[t & 1][2 * lane]) = cs;
+    if constexpr (KAD) {
+      const float2 cs = cos_sin_rev((double)(t * kTile) * rev_lane);
+      *reinterpret_cast<float2*>(&s_rot[t & 1][2 * lane]) = cs;
+    }
   };
   rot_table(0);
   rot_table(1);
@@ -155,7 +161,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   if (producer) {
     // per-lane part (producers): key offset 16 pw + lc within the tile, pairs 16cb + 4lg + jj
     float co[4][4], so[4][4];
-    {
+    if constexpr (KAD) {
       const double off = (double)(kBlock * pw + lc);
   #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
@@ -182,24 +188,28 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         tr.kbl[cb] = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
         tr.kbh[cb] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
       }
-      const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, on * kBlock * r * 2);
-      if constexpr (RP == 16) {
-        const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
-        tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
-      } else {
+      if constexpr (KAD) {
+        const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, on * kBlock * r * 2);
+        if constexpr (RP == 16) {
+          const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
+          tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
+        } else {
   #pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          tr.lk[kc] = bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
+          for (int kc = 0; kc < KC; ++kc)
+            tr.lk[kc] = bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
+        }
       }
       const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
                                on * D * kBlock * 2);
   #pragma unroll
       for (int u = 0; u < 4; ++u) tr.vv[u] = bld16(rv, ((2 * lane + (u >> 1)) * kBlock + 8 * (u & 1)) * 2);
-      const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, on * r * kBlock * 2);
+      if constexpr (VAD) {
+        const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, on * r * kBlock * 2);
   #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = lane + 64 * u, rank = e >> 1;
-        tr.lvv[u] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
+        for (int u = 0; u < 2; ++u) {
+          const int e = lane + 64 * u, rank = e >> 1;
+          tr.lvv[u] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
+        }
       }
     };
 
@@ -226,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         *reinterpret_cast<uint4*>(sv + (2 * lane + (u >> 1)) * kVPitch + kBlock * pw + 8 * (u & 1)) = v;
       }
   #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < (VAD ? 2 : 0); ++u) {
         const int e = lane + 64 * u;
         if (e < 2 * RP) {
           uint4 v = tr.lvv[u];
@@ -239,6 +249,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
           }
           *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
         }
+      }
+      if constexpr (!KAD) {  // no key adapter: the base keys as loaded
+  #pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+          *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) = tr.kbl[cb];
+          *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) = tr.kbh[cb];
+        }
+        return;
       }
       const float* rot = s_rot[t & 1];
   #pragma unroll
@@ -369,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
       }
     }
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) {
+    for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
         const uint16_t* lr = slv + (16 * rr + lc) * kVPitch + 32 * kp + 4 * lg;
@@ -434,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
 #pragma unroll
         for (int i = 0; i < 8; ++i) o[rt][i] *= alpha[rt];
 #pragma unroll
-        for (int i = 0; i < NRT; ++i) cacc[rt][i] *= alpha[rt];
+        for (int i = 0; i < (VAD ? NRT : 0); ++i) cacc[rt][i] *= alpha[rt];
       }
     }
   };
@@ -461,7 +479,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-    for (int rr = 0; rr < NRT; ++rr) {
+    for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
       float hi[4], lo[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -493,16 +511,35 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
 
 }  // namespace
 
+namespace {
+template <bool KAD, bool VAD>
+bool launch_rank(const PrefillArgs& a, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (a.rp) {
+    case 16: hipLaunchKernelGGL((prefill_bf16_kernel<16, KAD, VAD>), grid, block, 0, stream, a); return true;
+    case 32: hipLaunchKernelGGL((prefill_bf16_kernel<32, KAD, VAD>), grid, block, 0, stream, a); return true;
+    case 64: hipLaunchKernelGGL((prefill_bf16_kernel<64, KAD, VAD>), grid, block, 0, stream, a); return true;
+    default: return false;
+  }
+}
+}  // namespace
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const int n_work = a.Hkv * a.S * a.q_tiles;
   const int per = (n_work + kNumXcd - 1) / kNumXcd;
   const dim3 grid(per * kNumXcd), block(kThreads);
-  switch (a.rp) {
-    case 16: hipLaunchKernelGGL(prefill_bf16_kernel<16>, grid, block, 0, stream, a); break;
-    case 32: hipLaunchKernelGGL(prefill_bf16_kernel<32>, grid, block, 0, stream, a); break;
-    case 64: hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, stream, a); break;
-    default: return hipErrorInvalidValue;
+  const bool kad = a.bk != nullptr, vad = a.bv != nullptr;
+  bool launched;
+  if (kad && vad)
+    launched = launch_rank<true, true>(a, grid, block, stream);
+  else if (vad)
+    launched = launch_rank<false, true>(a, grid, block, stream);
+  else if (kad)
+    launched = launch_rank<true, false>(a, grid, block, stream);
+  else {  // no adapter: rank-free
+    hipLaunchKernelGGL((prefill_bf16_kernel<16, false, false>), grid, block, 0, stream, a);
+    launched = true;
   }
+  if (!launched) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

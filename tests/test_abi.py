@@ -52,7 +52,18 @@ def _decode(**over):
     (dict(d=64), B.LRA_ERR_UNSUPPORTED, "d = 128"),
     (dict(dtype=7), B.LRA_ERR_UNSUPPORTED, "dtype"),
     (dict(max_rank=65), B.LRA_ERR_UNSUPPORTED, "max_rank"),
-    (dict(max_rank=0), B.LRA_ERR_UNSUPPORTED, "max_rank"),
+    (dict(max_rank=0), B.LRA_ERR_INVALID_ARG, "max_rank"),
+    (dict(max_rank=-1), B.LRA_ERR_UNSUPPORTED, "max_rank"),
+    (dict(bk=None, bv=None), B.LRA_ERR_INVALID_ARG, "max_rank must be 0"),
+    (dict(lk=None), B.LRA_ERR_INVALID_ARG, "l_k_pools"),
+    (dict(bk=None, lk=None, lv=None), B.LRA_ERR_INVALID_ARG, "l_v_pools"),
+    (dict(ag=None), B.LRA_ERR_INVALID_ARG, "agent_ids"),
+    (dict(bv=None, ranks=None), B.LRA_ERR_INVALID_ARG, "ranks"),
+    # without adapters the agent and low-rank arguments may be NULL: the
+    # call gets past them to the workspace check
+    (dict(bk=None, bv=None, lk=None, lv=None, ag=None, ranks=None, max_rank=0, NA=0, wsb=100),
+     B.LRA_ERR_WORKSPACE, "workspace"),
+    (dict(bk=None, lk=None, wsb=100), B.LRA_ERR_WORKSPACE, "workspace"),
     (dict(bs=32), B.LRA_ERR_UNSUPPORTED, "block_size"),
     (dict(max_blocks=10), B.LRA_ERR_INVALID_ARG, "max_blocks"),
     (dict(ng=5), B.LRA_ERR_INVALID_ARG, "num_groups"),
@@ -85,6 +96,7 @@ def test_decode_workspace_is_small_and_bounded():
     assert sizes[-1] < (1 << 24) * 128 * 2
     assert f(4, 1, 32, 8, 128, 16, 8192, lra.LRA_F32) == 0  # fp32 path has no split
     assert f(4, 1, 30, 8, 128, 16, 8192, lra.LRA_BF16) == 0  # invalid sizes -> 0
+    assert f(4, 1, 32, 8, 128, 0, 8192, lra.LRA_BF16) == small  # no adapter plans as rank 16
 
 
 def test_build_rejects_bad_arguments():
@@ -114,3 +126,6 @@ def test_prefill_rejects_bad_arguments():
     assert call(mq=0) == B.LRA_ERR_INVALID_ARG
     assert call(mq=9000) == B.LRA_ERR_INVALID_ARG
     assert call(S=0) == B.LRA_OK
+    assert call(bk=None, bv=None) == B.LRA_ERR_INVALID_ARG  # max_rank must be 0 without adapters
+    assert call(bv=None, lv=None, lk=None) == B.LRA_ERR_INVALID_ARG
+    assert call(ag=None) == B.LRA_ERR_INVALID_ARG
