@@ -17,8 +17,10 @@ rocprofv3 counter summary when it was taken on the current kernel source.
 
 Other legs (same JSON line, under "legs"): the prefill chunk with its
 low-rank cache build, the 32-layer long-context decode, the 64-request
-serving mix and the tiny fp32 decode. ``cpu_baseline`` times the fp64
-oracle on the host on a bounded sample of the headline workload.
+serving mix, the tiny fp32 decode, and the 8B decode and prefill chunk
+without a key adapter (b_k NULL) and without adapters. ``cpu_baseline``
+times the fp64 oracle on the host on a bounded sample of the headline
+workload.
 """
 from __future__ import annotations
 
@@ -43,7 +45,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny")
+    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -76,6 +78,11 @@ def _timed(launch, K, W, n_copies):
     return t0.elapsed_time(t1) / K
 
 
+def _p(t):
+    """Device address of a tensor, 0 (NULL) for an absent one."""
+    return 0 if t is None else t.data_ptr()
+
+
 def _decode_caller(dw, ws_bytes):
     """Pre-marshalled C call of lora_attn_decode for each pool copy."""
     import torch
@@ -94,8 +101,8 @@ def _decode_caller(dw, ws_bytes):
     for kb, vb, lkp, lvp in copies:
         argsets.append((dw.q.data_ptr(), kb.data_ptr(), vb.data_ptr(), dw.block_tables.data_ptr(),
                         dw.block_tables.shape[1], dw.context_lens.data_ptr(), dw.max_context_len,
-                        dw.group_offsets.data_ptr(), ng, dw.agent_ids.data_ptr(), lkp.data_ptr(), lvp.data_ptr(),
-                        dw.bk_ptrs.data_ptr(), dw.bv_ptrs.data_ptr(), dw.ranks.data_ptr(), dw.max_rank, w.S,
+                        dw.group_offsets.data_ptr(), ng, _p(dw.agent_ids), _p(lkp), _p(lvp),
+                        _p(dw.bk_ptrs), _p(dw.bv_ptrs), _p(dw.ranks), dw.max_rank, w.S,
                         w.n_agents, w.Hq, w.Hkv, w.d, 16, w.sm_scale, w.theta, code, out.data_ptr(),
                         ws.data_ptr(), ws.numel(), stream))
 
@@ -122,9 +129,9 @@ def _replicate(dw, min_bytes):
         lvs = [t.clone() for t in dw.lv_pools]
         w = dw.w
         lkp = torch.tensor([lks[w.pool_of_agent[a]].data_ptr() for a in range(w.n_agents)], dtype=torch.int64,
-                           device="cuda")
+                           device="cuda") if w.has_k else None
         lvp = torch.tensor([lvs[w.pool_of_agent[a]].data_ptr() for a in range(w.n_agents)], dtype=torch.int64,
-                           device="cuda")
+                           device="cuda") if w.has_v else None
         keep += [lks, lvs]
         copies.append((kb, vb, lkp, lvp))
     dw.copies = copies
@@ -133,13 +140,16 @@ def _replicate(dw, min_bytes):
 
 
 def decode_bytes(w):
-    """Algorithmic bytes of one decode step: every distinct buffer once."""
+    """Algorithmic bytes of one decode step: every distinct buffer once (the
+    low-rank rows and B matrices of present adapters only)."""
     es = 2 if w.dtype == "bf16" else 4
+    n_proj = int(w.has_k) + int(w.has_v)
     tok_groups = sum(w.segments[i].T for i in range(len(w.segments)))
     base = tok_groups * w.Hkv * w.d * es * 2
-    lr = sum(w.segments[i].T * sum(w.pool_rank[p] for p in w.segments[i].pools) for i in range(len(w.segments))) * es * 2
-    used_agents = sorted({sq.agent for sq in w.seqs})
-    bmat = sum(w.ranks[a] * w.Hkv * w.d * es * 2 for a in used_agents)
+    lr = sum(w.segments[i].T * sum(w.pool_rank[p] for p in w.segments[i].pools)
+             for i in range(len(w.segments))) * es * n_proj
+    used_agents = sorted({sq.agent for sq in w.seqs if sq.agent >= 0})
+    bmat = sum(w.ranks[a] * w.Hkv * w.d * es * n_proj for a in used_agents)
     qo = w.S * w.Hq * w.d * es * 2
     tables = sum(-(-w.context_len(s) // 16) for s in range(w.S)) * 4 + w.S * 4 * 2
     return base + lr + bmat + qo + tables
@@ -148,15 +158,16 @@ def decode_bytes(w):
 def decode_flops(w):
     """Algorithmic FLOPs of one decode step over visible pairs: adapter key
     rebuild, QK, PV, P L_v and the final C B_v."""
-    G = w.Hq // w.Hkv
     f = 0
     for s in range(w.S):
         T = w.context_len(s)
-        r = w.ranks[w.seqs[s].agent]
-        f += 2 * T * r * w.Hkv * w.d  # rebuild L_k B_k (per agent, per KV head)
+        a = w.seqs[s].agent
+        rk = w.ranks[a] if (a >= 0 and w.has_k) else 0
+        rv = w.ranks[a] if (a >= 0 and w.has_v) else 0
+        f += 2 * T * rk * w.Hkv * w.d  # rebuild L_k B_k (per agent, per KV head)
         f += 2 * T * w.Hq * w.d * 2  # QK and PV
-        f += 2 * T * w.Hq * r  # P L_v
-        f += 2 * w.Hq * r * w.d  # C B_v
+        f += 2 * T * w.Hq * rv  # P L_v
+        f += 2 * w.Hq * rv * w.d  # C B_v
     return f
 
 
@@ -174,13 +185,16 @@ def _traffic(kernel_src, launches_per_step=1):
 
 
 # ------------------------------------------------------------------ legs
-def leg_decode(K, W):
+def leg_decode(K, W, adapt="kv"):
+    """The 8B-shaped decode; ``adapt`` "v" drops the key adapter (b_k NULL),
+    "none" both adapters."""
     from workloads import config_8b_decode
     from workloads.device import upload
 
     import shared_base_kv_amd as lra
 
     w = config_8b_decode()
+    w.adapt = adapt
     dw = upload(w)
     ncopy = _replicate(dw, 2 * MALL_BYTES)
     wsb = lra.lora_attn_decode_workspace_size(w.S, 1, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len, lra.LRA_BF16)
@@ -298,19 +312,41 @@ def leg_prefill(K, W):
                 tokens=sum(sq.q_len for sq in w.seqs), build_bytes=4 * 2 * (512 * 4096 * 2 + 4096 * 16 * 2 + 512 * 16 * 2))
 
 
+def leg_prefill_absent(K, W, adapt):
+    """The prefill chunk's attention alone with absent adapters."""
+    from workloads import config_prefill
+    from workloads.device import upload
+
+    import shared_base_kv_amd as lra
+
+    w = config_prefill()
+    w.adapt = adapt
+    dw = upload(w)
+    out = dw.new_out()
+
+    def prefill():
+        lra.lora_attn_prefill(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
+                              dw.cu_q_lens, dw.max_q_len, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs,
+                              dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out)
+
+    ms = _timed(lambda i: prefill(), max(4, K // 5), 2, 1)
+    return dict(prefill_ms=ms, flops=prefill_flops(w), tokens=sum(sq.q_len for sq in w.seqs))
+
+
 def prefill_flops(w):
     """Visible-pair FLOPs of the prefill chunk: QK, PV, P L_v over causal pairs,
-    the adapter key rebuild once per token, and C B_v per row."""
-    G = w.Hq // w.Hkv
+    the adapter key rebuild once per token, and C B_v per row (adapter terms
+    of present adapters only)."""
     f = 0
     for s, sq in enumerate(w.seqs):
         T = w.context_len(s)
-        r = w.ranks[sq.agent]
+        rk = w.ranks[sq.agent] if (sq.agent >= 0 and w.has_k) else 0
+        rv = w.ranks[sq.agent] if (sq.agent >= 0 and w.has_v) else 0
         nq = sq.q_len
         pairs = sum(T - nq + i + 1 for i in range(nq))
-        f += pairs * w.Hq * (2 * w.d * 2 + 2 * r)
-        f += 2 * T * r * w.Hkv * w.d
-        f += 2 * nq * w.Hq * r * w.d
+        f += pairs * w.Hq * (2 * w.d * 2 + 2 * rv)
+        f += 2 * T * rk * w.Hkv * w.d
+        f += 2 * nq * w.Hq * rv * w.d
     return f
 
 
@@ -431,6 +467,23 @@ def main():
             "hbm_frac": round(mx["bytes"] / (mx["kernel_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
             "bytes_per_step": mx["bytes"], "total_context": mx["total_context"]}
         log("serving-mix leg done")
+    for leg, adapt in (("qv", "v"), ("base", "none")):
+        if leg not in legs:
+            continue
+        d = leg_decode(K, W, adapt)
+        gbs = d["bytes"] / (d["kernel_ms"] / 1e3) / 1e9
+        extra[f"decode_{'no_key_adapter' if adapt == 'v' else 'no_adapter'}"] = {
+            "tokens_per_s": round(d["tokens"] / (d["step_ms"] / 1e3), 1),
+            "us_per_launch": round(d["kernel_ms"] * 1e3, 2), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": d["bytes"]}
+        if "prefill" in legs:
+            p = leg_prefill_absent(K, W, adapt)
+            tf = p["flops"] / (p["prefill_ms"] / 1e3) / 1e12
+            extra[f"prefill_{'no_key_adapter' if adapt == 'v' else 'no_adapter'}"] = {
+                "prefill_tokens_per_s": round(p["tokens"] / (p["prefill_ms"] / 1e3), 1),
+                "prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
+                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": p["flops"]}
+        log(f"{leg} legs done")
     if "tiny" in legs:
         ti = leg_tiny(K, W)
         extra["tiny_f32"] = {"us_per_step": round(ti["step_ms"] * 1e3, 2), "kernel_us": round(ti["kernel_ms"] * 1e3, 2)}

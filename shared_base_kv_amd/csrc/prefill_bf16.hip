@@ -445,6 +445,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         pop[rt][kp] = cat8(pack_bf16x4(pv_[2 * kp][0], pv_[2 * kp][1], pv_[2 * kp][2], pv_[2 * kp][3]),
                            pack_bf16x4(pv_[2 * kp + 1][0], pv_[2 * kp + 1][1], pv_[2 * kp + 1][2], pv_[2 * kp + 1][3]));
     }
+    // the probabilities and sums are formed here, in the block of the matrix
+    // products they can overlap, not sunk past the rescale branch
+    asm volatile("" ::"v"(pop[0][0]), "v"(pop[0][1]), "v"(pop[1][0]), "v"(pop[1][1]), "v"(l_run[0]), "v"(l_run[1]));
     // rescale the accumulators only when some row's running max moved
     if (__builtin_amdgcn_ballot_w64(alpha[0] != 1.f || alpha[1] != 1.f)) {
 #pragma unroll
@@ -456,22 +459,30 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
       }
     }
   };
-  auto softmax_tile = [&](int t) __attribute__((always_inline)) {
-    if (t * kTile + kTile - 1 > p0)
-      softmax(t, std::true_type{});
-    else
-      softmax(t, std::false_type{});
-  };
+  // tiles wholly at or before the first row's position need no mask; the
+  // two loops keep scores, P V and the softmax of one step in one basic
+  // block, so the softmax arithmetic can issue between the matrix products
+  const int n_plain = (p0 + 1) / kTile;
 
   __syncthreads();  // tile 0 is in LDS
   scores(0);
-  softmax_tile(0);
+  if (n_plain > 0)
+    softmax(0, std::false_type{});
+  else
+    softmax(0, std::true_type{});
   __syncthreads();  // scores of tile 0 are done and tile 1 is in LDS
-  for (int kt = 1; kt < n_tiles; ++kt) {
+  int kt = 1;
+  for (; kt < min(n_plain, n_tiles); ++kt) {
     scores(kt);
     pv(kt - 1);
-    softmax_tile(kt);
+    softmax(kt, std::false_type{});
     __syncthreads();  // keys of tile kt and values of tile kt - 1 are consumed; tile kt + 1 is in LDS
+  }
+  for (; kt < n_tiles; ++kt) {
+    scores(kt);
+    pv(kt - 1);
+    softmax(kt, std::true_type{});
+    __syncthreads();
   }
   pv(n_tiles - 1);
 
