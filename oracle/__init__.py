@@ -7,6 +7,7 @@ from .lra_oracle import (  # noqa: F401
     lora_attn_decode,
     lora_attn_prefill,
     lr_cache_build,
+    lr_cache_build_multi,
     materialise_kv,
     rope_angles,
     rope_rotate,

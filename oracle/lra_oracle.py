@@ -148,3 +148,12 @@ def lora_attn_prefill(seqs, *, sm_scale: float, theta: float) -> np.ndarray:
 def lr_cache_build(X: np.ndarray, A: np.ndarray) -> np.ndarray:
     """Low-rank cache rows L = X A (fp64), X [n, hidden], A [hidden, r]."""
     return np.asarray(X, np.float64) @ np.asarray(A, np.float64)
+
+
+def lr_cache_build_multi(X: np.ndarray, A: np.ndarray, group_cols) -> list:
+    """Low-rank rows of several adapters from one X (PReCache, Figure 1
+    caption, A1-A3): group g is X times columns group_cols[g]:group_cols[g+1]
+    of A, in fp64."""
+    L = lr_cache_build(X, A)
+    return [L[:, group_cols[g] : group_cols[g + 1]] for g in range(len(group_cols) - 1)]
+

@@ -267,4 +267,20 @@ def pin_lr_cache_build(o):
     assert np.array_equal(o.lr_cache_build(X, np.eye(7)), X)
 
 
+def pin_lr_cache_build_multi(o):
+    """Groups of uneven width each equal X times their own slice of A, by
+    scalar loops, and together cover every column once."""
+    rng = np.random.default_rng(11)
+    X = rng.standard_normal((4, 6))
+    A = rng.standard_normal((6, 7))
+    cols = [0, 2, 3, 7]
+    parts = o.lr_cache_build_multi(X, A, cols)
+    assert len(parts) == 3
+    for g, P in enumerate(parts):
+        c0, c1 = cols[g], cols[g + 1]
+        assert P.shape == (4, c1 - c0)
+        ref = [[sum(X[i][k] * A[k][c] for k in range(6)) for c in range(c0, c1)] for i in range(4)]
+        assert np.allclose(P, ref, atol=1e-13), g
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -11,6 +11,7 @@ _orig_rope = O.rope_rotate
 _orig_attend = O.attend
 _orig_adapter = O.adapter_term
 _orig_mat = O.materialise_kv
+_orig_multi = O.lr_cache_build_multi
 
 
 def _rope_sign(x, positions, theta):
@@ -93,6 +94,11 @@ def _no_scale(q, positions, K, V, sm_scale):
     return _orig_attend(q, positions, K, V, 1.0)
 
 
+def _multi_shifted(X, A, group_cols):
+    L = _orig_multi(X, A, group_cols)
+    return [L[0]] + [np.roll(P, 1, axis=1) for P in L[1:]]
+
+
 def _build_transposed(X, A):
     return (np.asarray(A, np.float64).T @ np.asarray(X, np.float64).T).T[:, ::-1]
 
@@ -113,6 +119,7 @@ MUTATIONS = {
     "causal_off_by_one": ("attend", _causal_exclusive),
     "missing_softmax_scale": ("attend", _no_scale),
     "build_columns_reversed": ("lr_cache_build", _build_transposed),
+    "multi_build_group_columns_shifted": ("lr_cache_build_multi", _multi_shifted),
 }
 
 
