@@ -92,8 +92,8 @@ const char* lra_last_error(void);
  *   slot_mapping != NULL: int64 [n_tokens]; row i goes to slot
  *   slot_mapping[i] of a paged pool laid out as `l_layout` says; a negative
  *   slot skips the row. Columns [0, n_cols) of each row are written.
- *   dtype: LRA_BF16. hidden % 8 == 0, 1 <= n_cols <= 256, ldx, lda >= their
- *   widths, X and A 16-byte aligned with ldx % 8 == 0.
+ *   dtype: LRA_BF16. hidden % 8 == 0, 1 <= n_cols <= 512, ldx, lda >= their
+ *   widths, X 16-byte aligned with ldx % 8 == 0.
  *   workspace: at least lr_cache_build_workspace_size(...) bytes of device
  *   memory (fp32 partial sums; contents on entry do not matter).
  * ---------------------------------------------------------------------- */
@@ -102,6 +102,31 @@ size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n
 int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void* L, int64_t ldl,
                    const int64_t* slot_mapping, int32_t l_layout, int32_t n_tokens, int32_t hidden,
                    int32_t n_cols, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Low-rank caches of several adapters from one pass over X (PReCache,
+ * Figure 1 caption, A1-A3: the hidden states produced when a context
+ * segment is first processed build the low-rank caches of every agent).
+ * A holds the adapters' down-projections side by side: columns
+ * [group_cols[g], group_cols[g+1]) form group g (say agent a's A_k, then its
+ * A_v), of width r_g. Row i of X A, restricted to group g, goes to slot
+ * slot_mapping[i] of the pool group_pools[g], laid out as group_layouts[g]
+ * says with n_cols = r_g (token-major [NB,16,r_g] or rank-major [NB,r_g,16]);
+ * a negative slot skips the row. Every column of X A is formed exactly as
+ * lr_cache_build forms it (same sums in the same order), so each group's
+ * rows are bit-identical to a separate lr_cache_build of that group, while X
+ * is read once for all of them.
+ *   group_cols (host) int32 [n_groups+1], group_cols[0] = 0, strictly
+ *   increasing, group_cols[n_groups] = n_cols. group_pools (host) [n_groups]
+ *   device pointers; group_layouts (host) int32 [n_groups] of lra_l_layout.
+ *   1 <= n_groups <= 64. slot_mapping: int64 [n_tokens], required.
+ *   Sizes, dtype and workspace as for lr_cache_build (the workspace query is
+ *   lr_cache_build_workspace_size with the total n_cols).
+ * ---------------------------------------------------------------------- */
+int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda, int32_t n_groups,
+                         const int32_t* group_cols, void* const* group_pools, const int32_t* group_layouts,
+                         const int64_t* slot_mapping, int32_t n_tokens, int32_t hidden, int32_t n_cols,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * Decode attention: one query token per sequence at position T_s - 1 over

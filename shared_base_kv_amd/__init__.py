@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     lora_attn_prefill,
     lora_attn_prefill_workspace_size,
     lr_cache_build,
+    lr_cache_build_multi,
     lr_cache_build_workspace_size,
     lra_last_error,
     lra_version,

@@ -29,6 +29,7 @@ EXPORTS = (
     "lra_last_error",
     "lr_cache_build_workspace_size",
     "lr_cache_build",
+    "lr_cache_build_multi",
     "lora_attn_decode_workspace_size",
     "lora_attn_decode",
     "lora_attn_prefill_workspace_size",
@@ -65,6 +66,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lr_cache_build_workspace_size.argtypes = [_i32, _i32, _i32]
     lib.lr_cache_build.restype = ctypes.c_int
     lib.lr_cache_build.argtypes = [_p, _i64, _p, _i64, _p, _i64, _p, _i32, _i32, _i32, _i32, _i32, _p, _sz, _p]
+    lib.lr_cache_build_multi.restype = ctypes.c_int
+    lib.lr_cache_build_multi.argtypes = [_p, _i64, _p, _i64, _i32, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _p, _sz, _p]
     size8 = [_i32] * 8
     lib.lora_attn_decode_workspace_size.restype = _sz
     lib.lora_attn_decode_workspace_size.argtypes = size8
@@ -136,6 +139,23 @@ def lr_cache_build(X, A, L, workspace, *, slot_mapping=None, l_layout=LRA_L_TOKE
                                  l_layout, n, hidden, n_cols, _dtype_code(X), _ptr(workspace),
                                  workspace.numel() * workspace.element_size() if workspace is not None else 0,
                                  _stream(stream)))
+
+
+def lr_cache_build_multi(X, A, group_cols, group_pools, group_layouts, slot_mapping, workspace, stream=None):
+    """Every group's low-rank rows from one pass over X: columns
+    group_cols[g]:group_cols[g+1] of X A go to pool group_pools[g] (a bf16
+    tensor or device address) in layout group_layouts[g], through the int64
+    slot mapping. X [n, hidden] and A [hidden, n_cols] bf16 tensors."""
+    n, hidden = X.shape
+    ng = len(group_pools)
+    cols = (ctypes.c_int32 * (ng + 1))(*group_cols)
+    pools = (ctypes.c_void_p * ng)(*[_ptr(p) for p in group_pools])
+    lays = (ctypes.c_int32 * ng)(*group_layouts)
+    _check(load().lr_cache_build_multi(_ptr(X), X.stride(0), _ptr(A), A.stride(0), ng, cols, pools, lays,
+                                       _ptr(slot_mapping), n, hidden, int(group_cols[-1]), _dtype_code(X),
+                                       _ptr(workspace),
+                                       workspace.numel() * workspace.element_size() if workspace is not None else 0,
+                                       _stream(stream)))
 
 
 def lora_attn_decode_workspace_size(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) -> int:

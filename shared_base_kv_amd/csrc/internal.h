@@ -65,15 +65,25 @@ struct DecodeArgs {
   double rope_rev[kMaxRopePairs];  // theta^(-2i/d) / (2 pi): revolutions per position, pair i
 };
 
+constexpr int kMaxBuildGroups = 64;  // destination column groups of one cache build
+constexpr int kMaxBuildCols = 512;   // columns of A in one cache build
+
+// One cache build: L = X A, columns [group_col[g], group_col[g+1]) of the
+// product going to destination g (a dense matrix or a paged pool).
 struct BuildArgs {
   const uint16_t* X;
   const uint16_t* A;
-  void* L;
   const int64_t* slot_mapping;
   float* partials;
-  int64_t ldx, lda, ldl;
-  int32_t n_tokens, hidden, n_cols, layout;
+  int64_t ldx, lda;
+  int32_t n_tokens, hidden, n_cols;
   int32_t ksplit, kchunk, row_tiles, col_tiles;
+  int32_t n_groups;
+  int32_t max_group_elems;  // max over groups of n_tokens * group width
+  int32_t group_col[kMaxBuildGroups + 1];
+  int32_t group_layout[kMaxBuildGroups];  // 0 token-major (row stride group_ld), 1 rank-major
+  int64_t group_ld[kMaxBuildGroups];
+  void* group_dst[kMaxBuildGroups];
 };
 
 struct PrefillArgs {

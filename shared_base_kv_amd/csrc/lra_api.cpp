@@ -139,48 +139,123 @@ size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n
   return (size_t)ksplit * n_tokens * n_cols * sizeof(float);
 }
 
+}  // extern "C"
+
+namespace lra {
+namespace {
+
+// Checks shared by the cache builds, then the launch. The group table
+// (columns, destinations, layouts, row strides) is already in `a`.
+int launch_build(BuildArgs& a, const char* name, int32_t dtype, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "%s supports LRA_BF16 only (got %d)", name, dtype);
+  if (!a.X || !a.A) return fail(LRA_ERR_INVALID_ARG, "%s: X and A must be non-null", name);
+  if (!aligned16(a.X) || a.ldx % 8) return fail(LRA_ERR_INVALID_ARG, "%s: X must be 16-byte aligned with ldx %% 8 == 0", name);
+  if (a.ldx < a.hidden || a.lda < a.n_cols)
+    return fail(LRA_ERR_INVALID_ARG, "%s: ldx (%lld) < hidden or lda (%lld) < n_cols", name, (long long)a.ldx,
+                (long long)a.lda);
+  const size_t need = lr_cache_build_workspace_size(a.n_tokens, a.hidden, a.n_cols);
+  if (!workspace || workspace_bytes < need)
+    return fail(LRA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", name, need, workspace_bytes);
+  a.partials = (float*)workspace;
+  a.row_tiles = ceil_div(a.n_tokens, 16);
+  a.col_tiles = ceil_div(a.n_cols, 16);
+  a.ksplit = (int)(need / ((size_t)a.n_tokens * a.n_cols * sizeof(float)));
+  a.kchunk = (int)round_up((size_t)ceil_div(a.hidden, a.ksplit), 32);
+  if (a.kchunk > 1024) return fail(LRA_ERR_UNSUPPORTED, "internal: hidden chunk %d too large", a.kchunk);
+  int widest = 0;
+  for (int g = 0; g < a.n_groups; ++g) widest = widest > a.group_col[g + 1] - a.group_col[g] ? widest : a.group_col[g + 1] - a.group_col[g];
+  a.max_group_elems = a.n_tokens * widest;
+  const hipError_t e = launch_lr_build_bf16(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
+  return ok();
+}
+
+int check_build_sizes(const char* name, int32_t n_tokens, int32_t hidden, int32_t n_cols) {
+  if (n_tokens < 0 || hidden < 1 || n_cols < 1)
+    return fail(LRA_ERR_INVALID_ARG, "%s: bad sizes n_tokens=%d hidden=%d n_cols=%d", name, n_tokens, hidden, n_cols);
+  if (n_cols > kMaxBuildCols) return fail(LRA_ERR_UNSUPPORTED, "%s: n_cols must be <= %d (got %d)", name, kMaxBuildCols, n_cols);
+  if (hidden % 8) return fail(LRA_ERR_UNSUPPORTED, "%s: hidden must be a multiple of 8 (got %d)", name, hidden);
+  if ((long long)n_tokens * n_cols > (1LL << 30)) return fail(LRA_ERR_UNSUPPORTED, "%s: n_tokens * n_cols too large", name);
+  return LRA_OK;
+}
+
+}  // namespace
+}  // namespace lra
+
+extern "C" {
+
 int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void* L, int64_t ldl,
                    const int64_t* slot_mapping, int32_t l_layout, int32_t n_tokens, int32_t hidden,
                    int32_t n_cols, int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
   if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "lr_cache_build supports LRA_BF16 only (got %d)", dtype);
-  if (n_tokens < 0 || hidden < 1 || n_cols < 1)
-    return fail(LRA_ERR_INVALID_ARG, "bad sizes n_tokens=%d hidden=%d n_cols=%d", n_tokens, hidden, n_cols);
-  if (n_cols > 256) return fail(LRA_ERR_UNSUPPORTED, "n_cols must be <= 256 (got %d)", n_cols);
-  if (hidden % 8) return fail(LRA_ERR_UNSUPPORTED, "hidden must be a multiple of 8 (got %d)", hidden);
+  int rc = check_build_sizes("lr_cache_build", n_tokens, hidden, n_cols);
+  if (rc != LRA_OK) return rc;
   if (n_tokens == 0) return ok();
-  if (!X || !A || !L) return fail(LRA_ERR_INVALID_ARG, "X, A and L must be non-null");
-  if (!aligned16(X) || ldx % 8) return fail(LRA_ERR_INVALID_ARG, "X must be 16-byte aligned with ldx %% 8 == 0");
-  if (ldx < hidden || lda < n_cols) return fail(LRA_ERR_INVALID_ARG, "ldx (%lld) < hidden or lda (%lld) < n_cols", (long long)ldx, (long long)lda);
+  if (!L) return fail(LRA_ERR_INVALID_ARG, "lr_cache_build: L must be non-null");
   if (l_layout != LRA_L_TOKEN_MAJOR && l_layout != LRA_L_RANK_MAJOR)
     return fail(LRA_ERR_INVALID_ARG, "unknown l_layout %d", l_layout);
   if (!slot_mapping && l_layout != LRA_L_TOKEN_MAJOR)
     return fail(LRA_ERR_INVALID_ARG, "a dense store (no slot mapping) is token-major only");
   if (l_layout == LRA_L_TOKEN_MAJOR && ldl < n_cols)
     return fail(LRA_ERR_INVALID_ARG, "ldl (%lld) < n_cols (%d)", (long long)ldl, n_cols);
-  const size_t need = lr_cache_build_workspace_size(n_tokens, hidden, n_cols);
-  if (!workspace || workspace_bytes < need)
-    return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need, workspace_bytes);
   BuildArgs a{};
   a.X = (const uint16_t*)X;
   a.A = (const uint16_t*)A;
-  a.L = L;
   a.slot_mapping = slot_mapping;
-  a.partials = (float*)workspace;
   a.ldx = ldx;
   a.lda = lda;
-  a.ldl = ldl;
   a.n_tokens = n_tokens;
   a.hidden = hidden;
   a.n_cols = n_cols;
-  a.layout = l_layout;
-  a.row_tiles = ceil_div(n_tokens, 16);
-  a.col_tiles = ceil_div(n_cols, 16);
-  a.ksplit = (int)(need / ((size_t)n_tokens * n_cols * sizeof(float)));
-  a.kchunk = (int)round_up((size_t)ceil_div(hidden, a.ksplit), 32);
-  if (a.kchunk > 1024) return fail(LRA_ERR_UNSUPPORTED, "internal: hidden chunk %d too large", a.kchunk);
-  const hipError_t e = launch_lr_build_bf16(a, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lr_cache_build launch failed: %s", hipGetErrorString(e));
-  return ok();
+  a.n_groups = 1;
+  a.group_col[0] = 0;
+  a.group_col[1] = n_cols;
+  a.group_layout[0] = l_layout;
+  a.group_ld[0] = ldl;
+  a.group_dst[0] = L;
+  return launch_build(a, "lr_cache_build", dtype, workspace, workspace_bytes, stream);
+}
+
+int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda, int32_t n_groups,
+                         const int32_t* group_cols, void* const* group_pools, const int32_t* group_layouts,
+                         const int64_t* slot_mapping, int32_t n_tokens, int32_t hidden, int32_t n_cols,
+                         int32_t dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "lr_cache_build_multi supports LRA_BF16 only (got %d)", dtype);
+  int rc = check_build_sizes("lr_cache_build_multi", n_tokens, hidden, n_cols);
+  if (rc != LRA_OK) return rc;
+  if (n_groups < 1 || n_groups > kMaxBuildGroups)
+    return fail(LRA_ERR_UNSUPPORTED, "n_groups must be in 1..%d (got %d)", kMaxBuildGroups, n_groups);
+  if (!group_cols || !group_pools || !group_layouts)
+    return fail(LRA_ERR_INVALID_ARG, "group_cols, group_pools and group_layouts must be non-null host arrays");
+  if (group_cols[0] != 0 || group_cols[n_groups] != n_cols)
+    return fail(LRA_ERR_INVALID_ARG, "group_cols must start at 0 and end at n_cols (%d)", n_cols);
+  for (int g = 0; g < n_groups; ++g) {
+    if (group_cols[g + 1] <= group_cols[g])
+      return fail(LRA_ERR_INVALID_ARG, "group %d is empty or group_cols is not increasing", g);
+    if (!group_pools[g]) return fail(LRA_ERR_INVALID_ARG, "group_pools[%d] is null", g);
+    if (group_layouts[g] != LRA_L_TOKEN_MAJOR && group_layouts[g] != LRA_L_RANK_MAJOR)
+      return fail(LRA_ERR_INVALID_ARG, "group_layouts[%d] = %d is not a layout", g, group_layouts[g]);
+  }
+  if (!slot_mapping) return fail(LRA_ERR_INVALID_ARG, "lr_cache_build_multi needs a slot mapping");
+  if (n_tokens == 0) return ok();
+  BuildArgs a{};
+  a.X = (const uint16_t*)X;
+  a.A = (const uint16_t*)A;
+  a.slot_mapping = slot_mapping;
+  a.ldx = ldx;
+  a.lda = lda;
+  a.n_tokens = n_tokens;
+  a.hidden = hidden;
+  a.n_cols = n_cols;
+  a.n_groups = n_groups;
+  for (int g = 0; g <= n_groups; ++g) a.group_col[g] = group_cols[g];
+  for (int g = 0; g < n_groups; ++g) {
+    a.group_layout[g] = group_layouts[g];
+    a.group_ld[g] = group_cols[g + 1] - group_cols[g];
+    a.group_dst[g] = group_pools[g];
+  }
+  return launch_build(a, "lr_cache_build_multi", dtype, workspace, workspace_bytes, stream);
 }
 
 // --------------------------------------------------------------------------

@@ -107,7 +107,7 @@ def test_build_rejects_bad_arguments():
     assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
     assert call(X=None) == B.LRA_ERR_INVALID_ARG
     assert call(hidden=4100, ldx=4100) == B.LRA_ERR_UNSUPPORTED
-    assert call(ncols=300, lda=300, ldl=300) == B.LRA_ERR_UNSUPPORTED
+    assert call(ncols=600, lda=600, ldl=600) == B.LRA_ERR_UNSUPPORTED
     assert call(lay=1) == B.LRA_ERR_INVALID_ARG  # rank-major needs a slot mapping
     assert call(ldl=8) == B.LRA_ERR_INVALID_ARG
     assert call(wsb=10) == B.LRA_ERR_WORKSPACE
@@ -129,3 +129,32 @@ def test_prefill_rejects_bad_arguments():
     assert call(bk=None, bv=None) == B.LRA_ERR_INVALID_ARG  # max_rank must be 0 without adapters
     assert call(bv=None, lv=None, lk=None) == B.LRA_ERR_INVALID_ARG
     assert call(ag=None) == B.LRA_ERR_INVALID_ARG
+
+
+def test_multi_build_rejects_bad_group_tables():
+    import ctypes
+
+    lib = lra.load()
+
+    def call(cols=(0, 16, 32), pools=(FAKE, FAKE), lays=(0, 1), slot=FAKE, ncols=32, **o):
+        ng = len(pools)
+        c = (ctypes.c_int32 * len(cols))(*cols)
+        p = (ctypes.c_void_p * ng)(*pools)
+        la = (ctypes.c_int32 * len(lays))(*lays)
+        args = dict(X=FAKE, ldx=4096, A=FAKE, lda=ncols, ng=o.pop("ng", ng), cols=c, pools=p, lays=la, slot=slot,
+                    n=512, hidden=4096, ncols=ncols, dtype=lra.LRA_BF16, ws=FAKE, wsb=o.pop("wsb", 1 << 30),
+                    stream=None)
+        args.update(o)
+        return lib.lr_cache_build_multi(*args.values())
+
+    assert call(cols=(0, 16, 30)) == B.LRA_ERR_INVALID_ARG  # does not end at n_cols
+    assert call(cols=(0, 0, 32)) == B.LRA_ERR_INVALID_ARG  # empty group
+    assert call(pools=(FAKE, None)) == B.LRA_ERR_INVALID_ARG
+    assert call(lays=(0, 5)) == B.LRA_ERR_INVALID_ARG
+    assert call(slot=None) == B.LRA_ERR_INVALID_ARG
+    assert call(ng=0) == B.LRA_ERR_UNSUPPORTED
+    assert call(ng=65) == B.LRA_ERR_UNSUPPORTED
+    assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
+    assert call(wsb=16) == B.LRA_ERR_WORKSPACE
+    assert call(n=0) == B.LRA_OK
+

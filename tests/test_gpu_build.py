@@ -64,3 +64,53 @@ def test_build_paged_stores_bit_exact():
     written = set(int(s) for s in slots if s >= 0)
     untouched = [s for s in range(nb * 16) if s not in written]
     assert not t[untouched].any() and not k[untouched].any()
+
+
+def _multi_case(n, hidden, ranks, seed):
+    """X, the side-by-side A of every (agent, k/v) group, group columns and layouts."""
+    widths = [r for r in ranks for _ in (0, 1)]  # agent a: A_k then A_v
+    cols = np.concatenate([[0], np.cumsum(widths)]).astype(np.int32).tolist()
+    X, A = build_inputs(n, hidden, cols[-1], seed=seed)
+    lays = [lra.LRA_L_TOKEN_MAJOR, lra.LRA_L_RANK_MAJOR] * len(ranks)
+    return X, A, cols, lays, widths
+
+
+@pytest.mark.parametrize("shape", [(512, 4096, (16, 16, 16, 16)), (300, 2048, (16, 8, 32, 64, 8)), (5, 520, (8,))])
+def test_multi_build_equals_single_builds_bit_exact(shape):
+    """Every group's pool rows from one multi-group build are bit-identical to
+    a separate lr_cache_build of that group's columns, and within the bf16
+    bound of the oracle's X A_g; skipped and unwritten slots stay untouched."""
+    n, hidden, ranks = shape
+    X, A, cols, lays, widths = _multi_case(n, hidden, ranks, seed=n + hidden)
+    nb = -(-n // 16) + 3
+    rng = np.random.default_rng(1)
+    slots = rng.permutation(nb * 16)[:n].astype(np.int64)
+    if n > 3:
+        slots[3] = -1
+    sm = torch.from_numpy(slots).cuda()
+    Xd, Ad = _dev_bf16(X), _dev_bf16(A)
+
+    def pools():
+        return [torch.zeros((nb, 16, w) if lay == 0 else (nb, w, 16), dtype=torch.bfloat16, device="cuda")
+                for w, lay in zip(widths, lays)]
+
+    multi = pools()
+    ws = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, cols[-1]), dtype=torch.uint8, device="cuda")
+    lra.lr_cache_build_multi(Xd, Ad, cols, multi, lays, sm, ws)
+    single = pools()
+    for g, (w, lay) in enumerate(zip(widths, lays)):
+        wsg = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, w), dtype=torch.uint8, device="cuda")
+        lra.lr_cache_build(Xd, Ad[:, cols[g]:cols[g + 1]], single[g], wsg, slot_mapping=sm, l_layout=lay, ldl=w,
+                           n_cols=w)
+    torch.cuda.synchronize()
+    refs = oracle.lr_cache_build_multi(X, A, cols)
+    for g, (w, lay) in enumerate(zip(widths, lays)):
+        m = multi[g].view(torch.int16).cpu().numpy()
+        assert np.array_equal(m, single[g].view(torch.int16).cpu().numpy()), g
+        rows = m.reshape(nb * 16, w) if lay == 0 else m.transpose(0, 2, 1).reshape(nb * 16, w)
+        got = multi[g].float().cpu().numpy()
+        got = got.reshape(nb * 16, w) if lay == 0 else got.transpose(0, 2, 1).reshape(nb * 16, w)
+        keep = slots >= 0
+        assert row_rel_err(got[slots[keep]], refs[g][keep]) <= TOL_BF16, g
+        untouched = sorted(set(range(nb * 16)) - set(int(s) for s in slots[keep]))
+        assert not rows[untouched].any(), g
