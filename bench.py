@@ -17,8 +17,9 @@ rocprofv3 counter summary when it was taken on the current kernel source.
 
 Other legs (same JSON line, under "legs"): the prefill chunk with its
 low-rank cache build, the 32-layer long-context decode, the 64-request
-serving mix, the tiny fp32 decode, and the 8B decode and prefill chunk
-without a key adapter (b_k NULL) and without adapters. ``cpu_baseline``
+serving mix, the tiny fp32 decode, the 8B decode and prefill chunk
+without a key adapter (b_k NULL) and without adapters, and the low-rank
+caches of 4 agents built from one segment's hidden states in one call. ``cpu_baseline``
 times the fp64 oracle on the host on a bounded sample of the headline
 workload.
 """
@@ -45,7 +46,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base")
+    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base,lrmulti")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -333,6 +334,45 @@ def leg_prefill_absent(K, W, adapt):
     return dict(prefill_ms=ms, flops=prefill_flops(w), tokens=sum(sq.q_len for sq in w.seqs))
 
 
+def leg_lr_multi(K, W, n_agents=4, rank=16):
+    """Low-rank caches of every agent from one segment's hidden states: X
+    [512, 4096] against the 2 * n_agents adapters' A (r=16 each) side by side,
+    one lr_cache_build_multi call into 2 * n_agents paged pools, against the
+    same rows built by one lr_cache_build call per adapter."""
+    import torch
+
+    import shared_base_kv_amd as lra
+    from workloads import bf16_bits, build_inputs
+
+    n, hidden = 512, 4096
+    ncols = 2 * n_agents * rank
+    X, A = build_inputs(n, hidden, ncols, seed=300)
+    dev = lambda x: torch.from_numpy(bf16_bits(x).view("int16")).view(torch.bfloat16).cuda()  # noqa: E731
+    Xd, Ad = dev(X), dev(A)
+    nb = n // 16 + 8
+    slots = torch.randperm(nb * 16, generator=torch.Generator().manual_seed(1))[:n].cuda()
+    cols = [rank * g for g in range(2 * n_agents + 1)]
+    lays = [lra.LRA_L_TOKEN_MAJOR, lra.LRA_L_RANK_MAJOR] * n_agents
+    pools = [torch.zeros((nb, 16, rank) if l == 0 else (nb, rank, 16), dtype=torch.bfloat16, device="cuda")
+             for l in lays]
+    ws = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, ncols), dtype=torch.uint8, device="cuda")
+    ws1 = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, rank), dtype=torch.uint8, device="cuda")
+
+    def multi():
+        lra.lr_cache_build_multi(Xd, Ad, cols, pools, lays, slots, ws)
+
+    def singles():
+        for g in range(2 * n_agents):
+            lra.lr_cache_build(Xd, Ad[:, cols[g]:cols[g + 1]], pools[g], ws1, slot_mapping=slots, l_layout=lays[g],
+                               ldl=rank, n_cols=rank)
+
+    kk = max(10, K)
+    ms_multi = _timed(lambda i: multi(), kk, 3, 1)
+    ms_single = _timed(lambda i: singles(), kk, 3, 1)
+    nbytes = n * hidden * 2 + hidden * ncols * 2 + n * ncols * 2 + n * 8  # X once, A, L rows, slot mapping
+    return dict(ms_multi=ms_multi, ms_single=ms_single, bytes=nbytes, n_groups=2 * n_agents, n_cols=ncols)
+
+
 def prefill_flops(w):
     """Visible-pair FLOPs of the prefill chunk: QK, PV, P L_v over causal pairs,
     the adapter key rebuild once per token, and C B_v per row (adapter terms
@@ -484,6 +524,14 @@ def main():
                 "prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": p["flops"]}
         log(f"{leg} legs done")
+    if "lrmulti" in legs:
+        lm = leg_lr_multi(K, W)
+        gbs = lm["bytes"] / (lm["ms_multi"] / 1e3) / 1e9
+        extra["lr_cache_build_multi_4_agents"] = {
+            "us_per_call": round(lm["ms_multi"] * 1e3, 2), "groups": lm["n_groups"], "n_cols": lm["n_cols"],
+            "us_per_adapter_calls": round(lm["ms_single"] * 1e3, 2), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": lm["bytes"]}
+        log("multi-adapter cache build leg done")
     if "tiny" in legs:
         ti = leg_tiny(K, W)
         extra["tiny_f32"] = {"us_per_step": round(ti["step_ms"] * 1e3, 2), "kernel_us": round(ti["kernel_ms"] * 1e3, 2)}

@@ -49,12 +49,27 @@ __global__ __launch_bounds__(256) void lr_build_partial_kernel(const BuildArgs a
     xf[i] = kok ? as_bf16x8(ld16(xrow + kk + 8 * lg)) : as_bf16x8(make_uint4(0, 0, 0, 0));
   }
 
+  // A rows can be read 8 columns at a time when every row start is 16-byte aligned
+  const bool a_vec = ((reinterpret_cast<uintptr_t>(a.A) & 15) == 0) && (a.lda % 8 == 0);
   for (int ct = 0; ct < a.col_tiles; ++ct) {
     __syncthreads();
-    for (int e = tid; e < 16 * kpad; e += 256) {
-      const int kk = e >> 4, col = e & 15;
-      const int gc = ct * 16 + col;
-      sAt[col][kk] = (kk < kn && gc < a.n_cols) ? a.A[(size_t)(k0 + kk) * a.lda + gc] : (uint16_t)0;
+    if (a_vec) {
+      // one 16-byte load per (k, 8 columns), transposed into A^T[col][k] in LDS
+      for (int e = tid; e < 2 * kpad; e += 256) {
+        const int kk = e >> 1, c8 = 8 * (e & 1);
+        const int gc = ct * 16 + c8;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (kk < kn && gc < a.n_cols) v = ld16(a.A + (size_t)(k0 + kk) * a.lda + gc);
+        const uint16_t* pv = reinterpret_cast<const uint16_t*>(&v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sAt[c8 + j][kk] = (gc + j < a.n_cols) ? pv[j] : (uint16_t)0;
+      }
+    } else {
+      for (int e = tid; e < 16 * kpad; e += 256) {
+        const int kk = e >> 4, col = e & 15;
+        const int gc = ct * 16 + col;
+        sAt[col][kk] = (kk < kn && gc < a.n_cols) ? a.A[(size_t)(k0 + kk) * a.lda + gc] : (uint16_t)0;
+      }
     }
     __syncthreads();
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
