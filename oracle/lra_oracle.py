@@ -30,7 +30,9 @@ Readings taken where the pages are silent (each is listed in the design doc):
   a chunk of q_len new tokens sits at T - q_len + i and sees keys 0..position;
 * softmax scale is an explicit argument (1/sqrt(d) unless stated);
 * a projection without an adapter (B = None) keeps its base cache unchanged,
-  and a sequence without an agent has neither adapter.
+  and a sequence without an agent has neither adapter;
+* an activation position a (default 0) leaves tokens n < a without adapter
+  terms in both K and V; queries are not affected by it.
 
 Everything is evaluated in float64 with materialised full-dimension K and V
 and a plain two-pass softmax: this file is the definition, not a fast path.
@@ -72,11 +74,16 @@ def adapter_term(l_rows: np.ndarray, b: np.ndarray, Hkv: int, d: int) -> np.ndar
     return (np.asarray(l_rows, np.float64) @ np.asarray(b, np.float64)).reshape(-1, Hkv, d)
 
 
-def materialise_kv(kb, vb, lk, lv, bk, bv, theta: float):
+def materialise_kv(kb, vb, lk, lv, bk, bv, theta: float, adapter_start: int = 0):
     """Full keys and values of one sequence.
 
     kb, vb [T, Hkv, d] base rows; lk, lv [T, r] low-rank rows; bk, bv [r, Hkv*d].
-    K[n] = kb[n] + rope_n(lk[n] bk),  V[n] = vb[n] + lv[n] bv.
+    K[n] = kb[n] + rope_n(lk[n] bk),  V[n] = vb[n] + lv[n] bv   for n >= adapter_start,
+    K[n] = kb[n],                     V[n] = vb[n]              for n <  adapter_start.
+    The activation position follows "Efficient Multi-Adapter LLM Serving via
+    Cross-Model KV-Cache Reuse with Activated LoRA" (abstract): an activated
+    adapter acts only on the tokens from its invocation point on, so the
+    cache before that point is the base model's.
 
     A projection without an adapter passes None for its B (and L): its cache
     is the base part alone. PReCache, appendix Table 13 caption, compares
@@ -87,10 +94,11 @@ def materialise_kv(kb, vb, lk, lv, bk, bv, theta: float):
     T, Hkv, d = kb.shape
     K = np.array(kb, dtype=np.float64)
     V = np.array(vb, dtype=np.float64)
+    on = (np.arange(T) >= adapter_start)[:, None, None]
     if bk is not None:
-        K = K + rope_rotate(adapter_term(lk, bk, Hkv, d), np.arange(T), theta)
+        K = K + np.where(on, rope_rotate(adapter_term(lk, bk, Hkv, d), np.arange(T), theta), 0.0)
     if bv is not None:
-        V = V + adapter_term(lv, bv, Hkv, d)
+        V = V + np.where(on, adapter_term(lv, bv, Hkv, d), 0.0)
     return K, V
 
 
@@ -116,18 +124,20 @@ def attend(q: np.ndarray, positions: np.ndarray, K: np.ndarray, V: np.ndarray, s
     return out
 
 
-def lora_attention(q, kb, vb, lk, lv, bk, bv, *, sm_scale: float, theta: float, q_positions=None):
+def lora_attention(q, kb, vb, lk, lv, bk, bv, *, sm_scale: float, theta: float, q_positions=None,
+                   adapter_start: int = 0):
     """Attention of one sequence's query rows over its shared-base + low-rank cache.
 
     q [nq, Hq, d]; the cache holds T = kb.shape[0] tokens. Default positions
     are the last nq positions (T - nq .. T - 1): one row is a decode step,
-    nq rows are a prefill chunk appended at the end of the context.
+    nq rows are a prefill chunk appended at the end of the context. Tokens
+    before adapter_start carry no adapter term.
     """
     T = kb.shape[0]
     nq = q.shape[0]
     if q_positions is None:
         q_positions = np.arange(T - nq, T)
-    K, V = materialise_kv(kb, vb, lk, lv, bk, bv, theta)
+    K, V = materialise_kv(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     return attend(np.asarray(q, np.float64), q_positions, K, V, sm_scale)
 
 

@@ -58,7 +58,8 @@ def oracle_rows(w, seqs, q_rows=None):
         else:
             rows = np.asarray(q_rows[s])
             pos = T - nq + rows
-            K, V = oracle.materialise_kv(lg["kb"], lg["vb"], lg["lk"], lg["lv"], lg["bk"], lg["bv"], w.theta)
+            K, V = oracle.materialise_kv(lg["kb"], lg["vb"], lg["lk"], lg["lv"], lg["bk"], lg["bv"], w.theta,
+                                         lg["adapter_start"])
             outs.append(oracle.attend(lg["q"][rows], pos, K, V, w.sm_scale))
     return outs
 

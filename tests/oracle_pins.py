@@ -143,6 +143,33 @@ def pin_absent_adapters_sdpa(o):
             assert np.allclose(got, ref, atol=1e-12, rtol=0), (nq, theta, np.abs(got - ref).max())
 
 
+def pin_adapter_start(o):
+    """Activation position a: start 0 is the full adapter, start T is the base
+    cache alone (SDPA over kb, vb), and in between the cache is kb, vb on
+    rows n < a and kb + lk bk, vb + lv bv on rows n >= a (rotary off, SDPA);
+    with rotary on, the rows from a on still carry their rotation at their
+    own absolute position (equal to the full oracle there)."""
+    rng = np.random.default_rng(12)
+    c = _rand_case(rng, T=12, Hq=6, Hkv=3, d=4, r=2, nq=3)
+    T, Hkv, d = c["kb"].shape
+    pos = np.arange(T - 3, T)
+    full = o.lora_attention(**c, sm_scale=0.5, theta=1e4)
+    assert np.array_equal(o.lora_attention(**c, sm_scale=0.5, theta=1e4, adapter_start=0), full)
+    base = o.lora_attention(**c, sm_scale=0.5, theta=1e4, adapter_start=T)
+    assert np.allclose(base, _sdpa(c["q"], c["kb"], c["vb"], pos, 0.5), atol=1e-12, rtol=0)
+    for a in (1, 5, 11):
+        K = c["kb"].copy()
+        V = c["vb"].copy()
+        K[a:] += (c["lk"][a:] @ c["bk"]).reshape(-1, Hkv, d)
+        V[a:] += (c["lv"][a:] @ c["bv"]).reshape(-1, Hkv, d)
+        got = o.lora_attention(**c, sm_scale=0.5, theta=0.0, adapter_start=a)
+        assert np.allclose(got, _sdpa(c["q"], K, V, pos, 0.5), atol=1e-12, rtol=0), a
+        Kf, Vf = o.materialise_kv(c["kb"], c["vb"], c["lk"], c["lv"], c["bk"], c["bv"], 1e4)
+        Ka, Va = o.materialise_kv(c["kb"], c["vb"], c["lk"], c["lv"], c["bk"], c["bv"], 1e4, a)
+        assert np.array_equal(Ka[a:], Kf[a:]) and np.array_equal(Va[a:], Vf[a:])
+        assert np.array_equal(Ka[:a], c["kb"][:a]) and np.array_equal(Va[:a], c["vb"][:a])
+
+
 def pin_uniform_scores_mean(o):
     """q = 0 gives equal weights: out = mean_n V[n] = mean(vb) + mean(lv) bv."""
     rng = np.random.default_rng(4)

@@ -48,38 +48,59 @@ def _adapter_head_major(l_rows, b, Hkv, d):
     return (np.asarray(l_rows) @ np.asarray(b)).reshape(-1, d, Hkv).transpose(0, 2, 1)
 
 
-def _drop_v_adapter(kb, vb, lk, lv, bk, bv, theta):
-    K, _ = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+def _drop_v_adapter(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    K, _ = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     return K, np.asarray(vb, np.float64).copy()
 
 
-def _drop_k_adapter(kb, vb, lk, lv, bk, bv, theta):
-    _, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+def _drop_k_adapter(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    _, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     return np.asarray(kb, np.float64).copy(), V
 
 
-def _rope_on_v_too(kb, vb, lk, lv, bk, bv, theta):
-    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+def _rope_on_v_too(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     T, Hkv, d = kb.shape
     v_ad = V - vb
     return K, vb + O.rope_rotate(v_ad, np.arange(T), theta)
 
 
-def _absent_key_drops_value(kb, vb, lk, lv, bk, bv, theta):
-    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+def _absent_key_drops_value(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     return K, (np.asarray(vb, np.float64).copy() if bk is None else V)
 
 
-def _absent_key_rotates_base(kb, vb, lk, lv, bk, bv, theta):
-    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+def _absent_key_rotates_base(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     if bk is None:
         K = O.rope_rotate(np.asarray(kb, np.float64), np.arange(kb.shape[0]), theta)
     return K, V
 
 
-def _absent_value_drops_key(kb, vb, lk, lv, bk, bv, theta):
-    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta)
+def _absent_value_drops_key(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
     return (np.asarray(kb, np.float64).copy() if bv is None else K), V
+
+
+def _start_off_by_one(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    return _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start + 1 if adapter_start else 0)
+
+
+def _start_keys_only(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    K, _ = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
+    _, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, 0)
+    return K, V
+
+
+def _start_shifts_rotation(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    T, Hkv, d = kb.shape
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
+    if bk is not None and adapter_start:
+        a = adapter_start
+        k_ad = O.adapter_term(lk, bk, Hkv, d)[a:]
+        K = K.copy()
+        K[a:] = np.asarray(kb, np.float64)[a:] + O.rope_rotate(k_ad, np.arange(T - a), theta)
+    return K, V
 
 
 def _gqa_modulo(j, Hq, Hkv):
@@ -115,6 +136,9 @@ MUTATIONS = {
     "absent_key_adapter_drops_value_adapter": ("materialise_kv", _absent_key_drops_value),
     "absent_key_adapter_rotates_base_keys": ("materialise_kv", _absent_key_rotates_base),
     "absent_value_adapter_drops_key_adapter": ("materialise_kv", _absent_value_drops_key),
+    "adapter_start_off_by_one": ("materialise_kv", _start_off_by_one),
+    "adapter_start_on_keys_only": ("materialise_kv", _start_keys_only),
+    "adapter_start_rotation_relative": ("materialise_kv", _start_shifts_rotation),
     "gqa_modulo_mapping": ("kv_head_of", _gqa_modulo),
     "causal_off_by_one": ("attend", _causal_exclusive),
     "missing_softmax_scale": ("attend", _no_scale),

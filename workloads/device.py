@@ -33,6 +33,7 @@ class DeviceWorkload:
     context_lens: torch.Tensor
     group_offsets: torch.Tensor
     agent_ids: torch.Tensor  # None without any adapter
+    adapter_start: torch.Tensor  # int32 [S] activation positions, None when all are 0
     lk_pools: list
     lv_pools: list
     bk: list
@@ -80,6 +81,8 @@ def upload(w: Workload, device="cuda", poison: bool = False, host_pools=None) ->
         block_tables=i32(w.block_tables()), context_lens=i32(ctx),
         group_offsets=i32(w.group_offsets) if w.group_offsets is not None else None,
         agent_ids=i32([sq.agent for sq in w.seqs]) if adapted else None,
+        adapter_start=(i32([sq.adapter_start for sq in w.seqs])
+                       if adapted and any(sq.adapter_start for sq in w.seqs) else None),
         lk_pools=lk_pools, lv_pools=lv_pools, bk=bk, bv=bv,
         lk_ptrs=ptrs(lk_of_agent) if w.has_k else None, lv_ptrs=ptrs(lv_of_agent) if w.has_v else None,
         bk_ptrs=ptrs(bk) if w.has_k else None, bv_ptrs=ptrs(bv) if w.has_v else None,

@@ -95,6 +95,7 @@ class SeqSpec:
     segments: tuple  # segment ids, in token order
     agent: int
     q_len: int = 1  # decode: 1; prefill: number of new query tokens
+    adapter_start: int = 0  # first token position that carries the adapter terms
 
 
 @dataclass
@@ -211,7 +212,7 @@ class Workload:
         vb = np.concatenate([p[1] for p in parts]).astype(np.float64)
         qo = self.q_offsets()
         q = self.q_all()[qo[s] : qo[s + 1]].astype(np.float64)
-        out = dict(q=q, kb=kb, vb=vb, lk=None, lv=None, bk=None, bv=None)
+        out = dict(q=q, kb=kb, vb=vb, lk=None, lv=None, bk=None, bv=None, adapter_start=sq.adapter_start)
         if sq.agent >= 0:
             pool = self.pool_of_agent[sq.agent]
             bk, bv = self.adapter(sq.agent)
@@ -316,6 +317,7 @@ def decode_workload(
     spare_blocks=0,
     seed=0,
     adapt="kv",
+    adapter_starts=None,
 ):
     """Decode batch: groups of sequences; each group shares one base context.
 
@@ -337,7 +339,8 @@ def decode_workload(
         pools = sorted({pool_of_agent[agent_of_seq[s + i]] for i in range(gs) if agent_of_seq[s + i] >= 0})
         segments.append(Segment(T=T, pools=tuple(pools)))
         for i in range(gs):
-            seqs.append(SeqSpec(segments=(g,), agent=agent_of_seq[s + i]))
+            st = 0 if adapter_starts is None else int(adapter_starts[s + i])
+            seqs.append(SeqSpec(segments=(g,), agent=agent_of_seq[s + i], adapter_start=st))
         s += gs
         go.append(s)
     return Workload(
@@ -381,6 +384,7 @@ def prefill_workload(
     seed=0,
     adapt="kv",
     agents=None,
+    adapter_starts=None,
 ):
     """Prefill chunks: each agent appends ``q_lens[a]`` new tokens after one
     shared prefix; one shared-A low-rank pool; agent a's new rows live in its
@@ -396,8 +400,9 @@ def prefill_workload(
     base = len(segments)
     for a in range(A):
         segments.append(Segment(T=q_lens[a], pools=(0,)))
-    seqs = [SeqSpec(segments=((0,) if prefix else ()) + (base + a,), agent=agents[a], q_len=q_lens[a])
-            for a in range(A)]
+    starts = [0] * A if adapter_starts is None else [int(x) for x in adapter_starts]
+    seqs = [SeqSpec(segments=((0,) if prefix else ()) + (base + a,), agent=agents[a], q_len=q_lens[a],
+                    adapter_start=starts[a]) for a in range(A)]
     return Workload(
         name=name, dtype=dtype, Hq=Hq, Hkv=Hkv, d=d, theta=theta, ranks=[rank] * A,
         pool_of_agent=[0] * A, pool_rank=[rank], segments=segments, seqs=seqs,
