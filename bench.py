@@ -102,7 +102,7 @@ def _decode_caller(dw, ws_bytes):
     for kb, vb, lkp, lvp in copies:
         argsets.append((dw.q.data_ptr(), kb.data_ptr(), vb.data_ptr(), dw.block_tables.data_ptr(),
                         dw.block_tables.shape[1], dw.context_lens.data_ptr(), dw.max_context_len,
-                        dw.group_offsets.data_ptr(), ng, _p(dw.agent_ids), _p(lkp), _p(lvp),
+                        dw.group_offsets.data_ptr(), ng, _p(dw.agent_ids), _p(dw.adapter_start), _p(lkp), _p(lvp),
                         _p(dw.bk_ptrs), _p(dw.bv_ptrs), _p(dw.ranks), dw.max_rank, w.S,
                         w.n_agents, w.Hq, w.Hkv, w.d, 16, w.sm_scale, w.theta, code, out.data_ptr(),
                         ws.data_ptr(), ws.numel(), stream))
@@ -303,7 +303,8 @@ def leg_prefill(K, W):
     def prefill():
         lra.lora_attn_prefill(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
                               dw.cu_q_lens, dw.max_q_len, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs,
-                              dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out)
+                              dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out,
+                              adapter_start=dw.adapter_start)
 
     kk = max(4, K // 5)
     b_kern = _timed(lambda i: build_all(), kk, 2, 1)
@@ -328,7 +329,8 @@ def leg_prefill_absent(K, W, adapt):
     def prefill():
         lra.lora_attn_prefill(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
                               dw.cu_q_lens, dw.max_q_len, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs,
-                              dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out)
+                              dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out,
+                              adapter_start=dw.adapter_start)
 
     ms = _timed(lambda i: prefill(), max(4, K // 5), 2, 1)
     return dict(prefill_ms=ms, flops=prefill_flops(w), tokens=sum(sq.q_len for sq in w.seqs))

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LRA_VERSION 100
+#define LRA_VERSION 200
 
 typedef enum lra_status {
   LRA_OK = 0,
@@ -147,6 +147,14 @@ int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda,
  *                 an adapter (it attends over the base cache alone; PReCache
  *                 Figure 1 caption batches such adapter-free paths with
  *                 adapted ones).
+ *   adapter_start int32 [S] or NULL (all 0): the first token position of
+ *                 sequence s that carries the adapter terms; tokens before it
+ *                 keep the base key and value (the activation point of an
+ *                 activated adapter: Efficient Multi-Adapter LLM Serving via
+ *                 Cross-Model KV-Cache Reuse with Activated LoRA, abstract).
+ *                 Cache blocks wholly before every start of a tile skip the
+ *                 key rebuild, the low-rank loads and P L_v. Not read without
+ *                 adapters. Any value is valid: <= 0 means every token, >= T_s none.
  *   l_k_pools, l_v_pools
  *                 device arrays [N_agents] of device pointers to each agent's
  *                 low-rank pools ([NB,16,r_a] and [NB,r_a,16]). Agents with
@@ -189,7 +197,7 @@ size_t lora_attn_decode_workspace_size(int32_t S, int32_t num_groups, int32_t Hq
 int lora_attn_decode(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
                      int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
                      const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
-                     const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                     const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
                      const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
                      int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
                      int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);
@@ -203,9 +211,10 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
  *
  *   q, out        [cu_q_lens[S], Hq, d]; cu_q_lens int32 [S+1], q_len_s <= T_s.
  *   max_q_len     (host) >= every q_len_s.
- *   Everything else as for decode (no grouping; agent id -1 and NULL b_k /
- *   b_v as there: without a key adapter the key tiles are the base keys as
- *   stored, without a value adapter no rank-space accumulator is kept).
+ *   Everything else as for decode (no grouping; agent id -1, adapter_start
+ *   and NULL b_k / b_v as there: without a key adapter the key tiles are the
+ *   base keys as stored, without a value adapter no rank-space accumulator is
+ *   kept; key tiles wholly before the activation point skip the rebuild).
  *   dtype: LRA_BF16, d = 128.
  *   workspace     lora_attn_prefill_workspace_size(...) bytes (may be 0,
  *                 then workspace may be NULL).
@@ -216,7 +225,7 @@ size_t lora_attn_prefill_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int3
 int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
                       int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
                       const int32_t* cu_q_lens, int32_t max_q_len, const int32_t* agent_ids,
-                      const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                      const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
                       const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
                       int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
                       int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);

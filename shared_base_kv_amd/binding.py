@@ -71,7 +71,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     size8 = [_i32] * 8
     lib.lora_attn_decode_workspace_size.restype = _sz
     lib.lora_attn_decode_workspace_size.argtypes = size8
-    attn = [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
+    attn = [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _p, _p, _p, _p, _p, _p, _p, _i32, _i32, _i32,
             _i32, _i32, _i32, _i32, _f32, _f32, _i32, _p, _p, _sz, _p]
     lib.lora_attn_decode.restype = ctypes.c_int
     lib.lora_attn_decode.argtypes = attn
@@ -164,15 +164,17 @@ def lora_attn_decode_workspace_size(S, num_groups, Hq, Hkv, d, max_rank, max_con
 
 def lora_attn_decode(q, k_base, v_base, block_tables, context_lens, max_context_len, group_offsets, agent_ids,
                      l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, n_agents, Hkv, sm_scale, rope_theta, out,
-                     workspace, stream=None):
+                     workspace, stream=None, adapter_start=None):
     """Decode step. q/out [S, Hq, d]; pools and tables as in include/lra.h;
-    l_k_pools, l_v_pools, b_k, b_v are int64 device tensors of addresses."""
+    l_k_pools, l_v_pools, b_k, b_v are int64 device tensors of addresses
+    (None: that adapter is absent); adapter_start an int32 [S] tensor or None."""
     S, Hq, d = q.shape
     num_groups = (group_offsets.numel() - 1) if group_offsets is not None else S
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().lora_attn_decode(
         _ptr(q), _ptr(k_base), _ptr(v_base), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-        max_context_len, _ptr(group_offsets), num_groups, _ptr(agent_ids), _ptr(l_k_pools), _ptr(l_v_pools),
+        max_context_len, _ptr(group_offsets), num_groups, _ptr(agent_ids), _ptr(adapter_start), _ptr(l_k_pools),
+        _ptr(l_v_pools),
         _ptr(b_k), _ptr(b_v), _ptr(ranks), max_rank, S, n_agents, Hq, Hkv, d, 16, sm_scale, rope_theta,
         _dtype_code(q), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 
@@ -183,13 +185,14 @@ def lora_attn_prefill_workspace_size(S, Hq, Hkv, d, max_rank, max_q_len, max_con
 
 def lora_attn_prefill(q, k_base, v_base, block_tables, context_lens, max_context_len, cu_q_lens, max_q_len,
                       agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, n_agents, Hkv, sm_scale,
-                      rope_theta, out, workspace=None, stream=None):
+                      rope_theta, out, workspace=None, stream=None, adapter_start=None):
     """Prefill chunks. q/out [sum q_len, Hq, d]; cu_q_lens int32 [S+1]."""
     _, Hq, d = q.shape
     S = cu_q_lens.numel() - 1
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(load().lora_attn_prefill(
         _ptr(q), _ptr(k_base), _ptr(v_base), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
-        max_context_len, _ptr(cu_q_lens), max_q_len, _ptr(agent_ids), _ptr(l_k_pools), _ptr(l_v_pools),
+        max_context_len, _ptr(cu_q_lens), max_q_len, _ptr(agent_ids), _ptr(adapter_start), _ptr(l_k_pools),
+        _ptr(l_v_pools),
         _ptr(b_k), _ptr(b_v), _ptr(ranks), max_rank, S, n_agents, Hq, Hkv, d, 16, sm_scale, rope_theta,
         _dtype_code(q), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))

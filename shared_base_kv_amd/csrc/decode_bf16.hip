@@ -56,6 +56,7 @@ struct TileAgent {
   const uint16_t* bv;
   int r;
   int seq;
+  int start;  // activation position: tokens before it carry no adapter term
 };
 
 __device__ __forceinline__ const uint16_t* uniform_ptr(const uint16_t* p) {
@@ -156,6 +157,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   __shared__ float s_ml[2][HW][16];
   __shared__ int s_shared_l;
   __shared__ int s_lead;  // first agent slot of the tile with an adapter (its rows travel with the blocks)
+  __shared__ int s_start_min, s_start_max;  // activation positions over the tile's adapted slots
 
   // ---- work item; consecutive logical items are dealt to one XCD ----
   const int per = (a.n_work + kNumXcd - 1) / kNumXcd;
@@ -194,12 +196,15 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) B.kr[ks] = as_bf16x8(bld16(r, (lc * D + 8 * lg + 32 * ks) * 2));
   };
-  auto load_lv = [&](Blk<RP>& B, int bi, const uint16_t* lk0, const uint16_t* lv0, int r0)
+  // low-rank rows of a block are read only when some token of it is at or
+  // past the tile's first activation position st_lo
+  auto load_lv = [&](Blk<RP>& B, int bi, const uint16_t* lk0, const uint16_t* lv0, int r0, int st_lo)
                      __attribute__((always_inline)) {
     const bool ok = bi < nb;
+    const bool lok = ok && (t_begin + bi * kBlock + kBlock > st_lo);
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
     if constexpr (KAD) {
-      const auto rlk = buf_rsrc(lk0 + (size_t)phys * kBlock * r0, ok ? kBlock * r0 * 2 : 0);
+      const auto rlk = buf_rsrc(lk0 + (size_t)phys * kBlock * r0, lok ? kBlock * r0 * 2 : 0);
       if constexpr (RP == 16) {
         B.lk16 = bld8(rlk, (4 * lg < r0) ? (lc * r0 + 4 * lg) * 2 : kOob);
       } else {
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
       }
     }
     if constexpr (VAD) {
-      const auto rlv = buf_rsrc(lv0 + (size_t)phys * r0 * kBlock, ok ? r0 * kBlock * 2 : 0);
+      const auto rlv = buf_rsrc(lv0 + (size_t)phys * r0 * kBlock, lok ? r0 * kBlock * 2 : 0);
 #pragma unroll
       for (int rr = 0; rr < NRT; ++rr)
         B.lv[rr] = bld8(rlv, (16 * rr + lc < r0) ? ((16 * rr + lc) * kBlock + 4 * lg) * 2 : kOob);
@@ -236,16 +241,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // with an adapter; its low-rank rows travel with the blocks, and the
   // tile's pools count as shared when every adapted slot reads the lead's. ----
   if (ADAPT && wave == 0) {
-    int sh = 1, lead = -1;
+    int sh = 1, lead = -1, st_min = 0x7fffffff, st_max = 0;
     const uint16_t *lk0 = nullptr, *lv0 = nullptr;
     int r0 = 0;
     for (int al = 0; al < NA; ++al) {
-      TileAgent t{nullptr, nullptr, nullptr, nullptr, 0, 0};
+      TileAgent t{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
       if (al < ns) {
         const int seq = s0 + al;
         const int ag = sload(a.agent_ids + seq);
         t.seq = seq;
         if (ag >= 0) {
+          t.start = a.act ? sload(a.act + seq) : 0;
+          st_min = min(st_min, t.start);
+          st_max = max(st_max, t.start);
           if constexpr (KAD) {
             t.lk = (const uint16_t*)sload(a.lk + ag);
             t.bk = (const uint16_t*)sload(a.bk + ag);
@@ -270,6 +278,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     if (lane == 0) {
       s_shared_l = sh;
       s_lead = lead < 0 ? 0 : lead;
+      s_start_min = st_min;
+      s_start_max = st_max;
     }
   }
   if (KAD && tid < kMaxRopePairs) s_rev[tid] = rev_arg;
@@ -300,7 +310,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const uint16_t* lk0 = ADAPT ? uniform_ptr(s_agent[lead].lk) : nullptr;
   const uint16_t* lv0 = ADAPT ? uniform_ptr(s_agent[lead].lv) : nullptr;
   const int r0 = ADAPT ? uniform(s_agent[lead].r) : 0;
-  load_lv(bufA, wave, lk0, lv0, r0);
+  const int st_min = ADAPT ? uniform(s_start_min) : 0;  // blocks wholly before it skip the adapter work
+  const int st_max = ADAPT ? uniform(s_start_max) : 0;  // blocks from it on need no per-row mask
+  load_lv(bufA, wave, lk0, lv0, r0, st_min);
 
   // ---- (5) staged values into LDS (waits for the first keys and the
   // staging loads, not for the loads of step 4) ----
@@ -346,6 +358,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const bool shared_l = s_shared_l != 0;
   const int row_al = lc / G;  // agent slot of this lane's query row
   const bool row_ok = row_al < ns && lc < a.apt * G;
+  const int row_start = (ADAPT && row_al < NA) ? s_agent[row_al].start : 0;  // this row's activation position
   const uint16_t* qrow_p = s_q + lc * kQPitch;
   const uint16_t* qp_row = s_qp + lc * kQpPitch;
   const double rev_lane = KAD ? s_rev[lane] : 0.0;
@@ -373,7 +386,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // key rows (K) and value rows (V) separately
   auto load_agents = [&](AgentRows<RP, NA>& ar, int bi, bool keys, bool vals) __attribute__((always_inline)) {
     if (shared_l) return;  // every agent reads agent 0's rows, which travel with the block
-    const bool ok = bi < nb;
+    const bool ok = bi < nb && (t_begin + bi * kBlock + kBlock > st_min);
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
 #pragma unroll
     for (int al = 1; al < NA; ++al) {
@@ -493,17 +506,26 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
         }
       }
     };
+    // Activation positions: a block wholly before every row's position skips
+    // the adapter products; in a block that some row's position falls inside
+    // or after, tokens before that row's position are masked out of its
+    // adapter score and of its P L_v.
+    const bool blk_ad = tb + kBlock > st_min;
+    const bool blk_mask = tb < st_max;
+    const int on_from = row_start - tb - 4 * lg;  // token jj of this lane is on iff jj >= on_from
     if constexpr (KAD) {
-      if (shared_l) {
-        if (a.rope)
-          adapter(std::true_type{}, std::true_type{});
-        else
-          adapter(std::false_type{}, std::true_type{});
-      } else {
-        if (a.rope)
-          adapter(std::true_type{}, std::false_type{});
-        else
-          adapter(std::false_type{}, std::false_type{});
+      if (blk_ad) {
+        if (shared_l) {
+          if (a.rope)
+            adapter(std::true_type{}, std::true_type{});
+          else
+            adapter(std::false_type{}, std::true_type{});
+        } else {
+          if (a.rope)
+            adapter(std::true_type{}, std::false_type{});
+          else
+            adapter(std::false_type{}, std::false_type{});
+        }
       }
     }
     if constexpr (!kAgentAhead) load_agents(ar_here, bi, false, true);
@@ -511,6 +533,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 #pragma unroll
     for (int al = 1; al < NA; ++al)
       if (row_al == al) sad = sa[al];
+    if (KAD && blk_mask) {
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) sad[jj] = jj >= on_from ? sad[jj] : 0.f;
+    }
     // online softmax over the block's 16 tokens (base-2 domain)
     float sv[4];
     float mx = -INFINITY;
@@ -552,15 +578,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     for (int cb = 0; cb < 8; ++cb)
       o[cb] = mfma16(as_i16x4(make_uint2(B.vr[cb].x & m01, B.vr[cb].y & m23)), as_i16x4(pop), o[cb]);
     // C^T += L_v^T P^T (per agent pool; rows of other agents masked out)
-    if constexpr (VAD) {
+    if (VAD && blk_ad) {
+      uint2 popc = pop;
+      if (blk_mask)
+        popc = make_uint2(pop.x & ((0 >= on_from ? 0xFFFFu : 0u) | (1 >= on_from ? 0xFFFF0000u : 0u)),
+                          pop.y & ((2 >= on_from ? 0xFFFFu : 0u) | (3 >= on_from ? 0xFFFF0000u : 0u)));
       if (shared_l) {
 #pragma unroll
         for (int rr = 0; rr < NRT; ++rr)
-          acl[rr] = mfma16(as_i16x4(make_uint2(B.lv[rr].x & m01, B.lv[rr].y & m23)), as_i16x4(pop), acl[rr]);
+          acl[rr] = mfma16(as_i16x4(make_uint2(B.lv[rr].x & m01, B.lv[rr].y & m23)), as_i16x4(popc), acl[rr]);
       } else {
 #pragma unroll
         for (int al = 0; al < NA; ++al) {
-          const uint2 pm = (row_ok && row_al == al) ? pop : make_uint2(0, 0);
+          const uint2 pm = (row_ok && row_al == al) ? popc : make_uint2(0, 0);
 #pragma unroll
           for (int rr = 0; rr < NRT; ++rr) {
             const uint2 lvr = al == 0 ? B.lv[rr] : ar.lv[al > 0 ? al - 1 : 0][rr];
@@ -581,13 +611,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     const int bi = wave + k * kDecodeWaves;
     if constexpr (kAgentAhead) load_agents(ar, bi, true, true);
     load_k(bufB, bi + kDecodeWaves);
-    load_lv(bufB, bi + kDecodeWaves, lk0, lv0, r0);
+    load_lv(bufB, bi + kDecodeWaves, lk0, lv0, r0, st_min);
     __builtin_amdgcn_sched_barrier(0);  // nothing of the compute moves above these loads
     compute(bufA, ar, bi);
     if (k + 1 >= nmine) break;
     if constexpr (kAgentAhead) load_agents(ar, bi + kDecodeWaves, true, true);
     load_k(bufA, bi + 2 * kDecodeWaves);
-    load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0);
+    load_lv(bufA, bi + 2 * kDecodeWaves, lk0, lv0, r0, st_min);
     __builtin_amdgcn_sched_barrier(0);
     compute(bufB, ar, bi + kDecodeWaves);
   }

@@ -54,6 +54,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
   const float* lv = rv ? (const float*)a.lv[ag] : nullptr;
   const float* bk = rk ? (const float*)a.bk[ag] : nullptr;
   const float* bv = rv ? (const float*)a.bv[ag] : nullptr;
+  const int act = (ag >= 0 && a.act) ? a.act[s] : 0;  // tokens before it carry no adapter term
   const float* kb = (const float*)a.kb;
   const float* vb = (const float*)a.vb;
   const int T = a.context_lens[s];
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
       if (n < T) {
         const int phys = sPhys[t / kBlock], slot = n % kBlock;
         float x1 = 0.f, x2 = 0.f;
-        for (int k = 0; k < rk; ++k) {
+        for (int k = 0; k < (n >= act ? rk : 0); ++k) {
           const float l = lk[((size_t)phys * kBlock + slot) * rk + k];
           x1 = fmaf(l, bk[(size_t)k * HD + h * D + i], x1);
           x2 = fmaf(l, bk[(size_t)k * HD + h * D + i + HALF], x2);
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
       const int row = e / 64, k = e % 64;
       if (row < G && k < rv) {
         float v = accC[u] * sAlpha[row];
-        for (int t = 0; t < kChunk && n0 + t < T; ++t) {
+        for (int t = (act > n0 ? act - n0 : 0); t < kChunk && n0 + t < T; ++t) {
           const int phys = sPhys[t / kBlock];
           v = fmaf(sP[row][t], lv[((size_t)phys * rv + k) * kBlock + t % kBlock], v);
         }

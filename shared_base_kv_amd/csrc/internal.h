@@ -39,6 +39,7 @@ struct DecodeArgs {
   const int32_t* context_lens;
   const int32_t* group_offsets;
   const int32_t* agent_ids;
+  const int32_t* act;  // per-sequence activation position, or NULL (0)
   const void* const* lk;
   const void* const* lv;
   const void* const* bk;
@@ -94,6 +95,7 @@ struct PrefillArgs {
   const int32_t* context_lens;
   const int32_t* cu_q_lens;
   const int32_t* agent_ids;
+  const int32_t* act;  // per-sequence activation position, or NULL (0)
   const void* const* lk;
   const void* const* lv;
   const void* const* bk;

@@ -268,7 +268,7 @@ size_t lora_attn_decode_workspace_size(int32_t S, int32_t num_groups, int32_t Hq
 int lora_attn_decode(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
                      int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
                      const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
-                     const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                     const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
                      const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
                      int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
                      int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -300,6 +300,7 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   a.context_lens = context_lens;
   a.group_offsets = group_offsets;
   a.agent_ids = agent_ids;
+  a.act = (b_k || b_v) ? adapter_start : nullptr;
   a.lk = l_k_pools;
   a.lv = l_v_pools;
   a.bk = b_k;
@@ -340,7 +341,7 @@ size_t lora_attn_prefill_workspace_size(int32_t S, int32_t Hq, int32_t Hkv, int3
 int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
                       int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
                       const int32_t* cu_q_lens, int32_t max_q_len, const int32_t* agent_ids,
-                      const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
+                      const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools, const void* const* b_k,
                       const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
                       int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
                       int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -371,6 +372,7 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
   a.context_lens = context_lens;
   a.cu_q_lens = cu_q_lens;
   a.agent_ids = agent_ids;
+  a.act = (b_k || b_v) ? adapter_start : nullptr;
   a.lk = l_k_pools;
   a.lv = l_v_pools;
   a.bk = b_k;

@@ -111,6 +111,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   const uint16_t* bk = (KAD && ag >= 0) ? (const uint16_t*)a.bk[ag] : nullptr;
   const uint16_t* bv = (VAD && ag >= 0) ? (const uint16_t*)a.bv[ag] : nullptr;
   const int r = ag >= 0 ? a.ranks[ag] : 0;
+  // activation position: keys before it keep the base key and value
+  const int a_start = (ag >= 0 && a.act) ? a.act[s] : 0;
   const int HD = a.Hkv * D;
   const int* bt_row = a.block_tables + (size_t)s * a.max_blocks;
 
@@ -181,6 +183,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
       const bool valid = key0 < kv_end;
       const int phys = uniform(bt_row[valid ? key0 / kBlock : 0]);
       const int on = valid ? 1 : 0;
+      const int lon = (valid && key0 + kBlock > a_start) ? 1 : 0;  // low-rank rows needed
       const auto rk = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
                                on * kBlock * D * 2);
   #pragma unroll
@@ -189,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         tr.kbh[cb] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
       }
       if constexpr (KAD) {
-        const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, on * kBlock * r * 2);
+        const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, lon * kBlock * r * 2);
         if constexpr (RP == 16) {
           const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
           tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
@@ -204,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   #pragma unroll
       for (int u = 0; u < 4; ++u) tr.vv[u] = bld16(rv, ((2 * lane + (u >> 1)) * kBlock + 8 * (u & 1)) * 2);
       if constexpr (VAD) {
-        const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, on * r * kBlock * 2);
+        const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, lon * r * kBlock * 2);
   #pragma unroll
         for (int u = 0; u < 2; ++u) {
           const int e = lane + 64 * u, rank = e >> 1;
@@ -220,6 +223,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
       constexpr bool LAST = decltype(last_tag)::value;
       const int key0 = t * kTile + kBlock * pw;
+      const bool blk_ad = key0 + kBlock > a_start;  // some key of the block carries adapter terms
+      const bool straddle = blk_ad && key0 < a_start;
       uint16_t* sk = s_k[t & 1];
       uint16_t* sv = s_v[t % kVBufs];
       uint16_t* slv = s_lv[t % kVBufs];
@@ -240,23 +245,30 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         const int e = lane + 64 * u;
         if (e < 2 * RP) {
           uint4 v = tr.lvv[u];
-          if constexpr (LAST) {
+          if (LAST || straddle) {  // keys past the context or before the activation point
             const int kk = key0 + 8 * (e & 1);
             uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
   #pragma unroll
-            for (int p = 0; p < 4; ++p)
-              w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
+            for (int p = 0; p < 4; ++p) {
+              const int k1 = kk + 2 * p, k2 = k1 + 1;
+              w32[p] &= ((k1 >= a_start && (!LAST || k1 < T)) ? 0xFFFFu : 0u) |
+                        ((k2 >= a_start && (!LAST || k2 < T)) ? 0xFFFF0000u : 0u);
+            }
           }
           *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
         }
       }
-      if constexpr (!KAD) {  // no key adapter: the base keys as loaded
+      if (!KAD || !blk_ad) {  // no key adapter on this block: the base keys as loaded
   #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) = tr.kbl[cb];
           *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) = tr.kbh[cb];
         }
         return;
+      }
+      if (straddle && key0 + lc < a_start) {  // this lane's key is before the activation point
+  #pragma unroll
+        for (int kc = 0; kc < (RP == 64 ? 2 : 1); ++kc) tr.lk[kc] = make_uint4(0, 0, 0, 0);
       }
       const float* rot = s_rot[t & 1];
   #pragma unroll
@@ -388,6 +400,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     }
 #pragma unroll
     for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
+      if (t * kTile + kTile <= a_start) break;  // tile wholly before the activation point
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
         const uint16_t* lr = slv + (16 * rr + lc) * kVPitch + 32 * kp + 4 * lg;

@@ -30,7 +30,7 @@ def run_decode(dw, workspace=None, out=None):
     out = dw.new_out() if out is None else out
     lra.lora_attn_decode(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
                          dw.group_offsets, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs, dw.ranks,
-                         dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out, ws)
+                         dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out, ws, adapter_start=dw.adapter_start)
     torch.cuda.synchronize()
     return out
 
@@ -40,7 +40,8 @@ def run_prefill(dw, out=None):
     out = dw.new_out() if out is None else out
     lra.lora_attn_prefill(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
                           dw.cu_q_lens, dw.max_q_len, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs,
-                          dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out)
+                          dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out,
+                          adapter_start=dw.adapter_start)
     torch.cuda.synchronize()
     return out
 

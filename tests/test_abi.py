@@ -36,7 +36,7 @@ def test_version_matches_header():
 
 def _decode(**over):
     args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=512, ctx=FAKE, max_ctx=8192, go=FAKE, ng=1, ag=FAKE,
-                lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8, d=128, bs=16,
+                act=None, lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8, d=128, bs=16,
                 sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
     args.update(over)
     rc = lra.load().lora_attn_decode(*args.values())
@@ -118,7 +118,7 @@ def test_build_rejects_bad_arguments():
 def test_prefill_rejects_bad_arguments():
     lib = lra.load()
     base = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=600, ctx=FAKE, max_ctx=8704, cu=FAKE, mq=512, ag=FAKE,
-                lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8, d=128, bs=16,
+                act=None, lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8, d=128, bs=16,
                 sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE, ws=None, wsb=0, stream=None)
     call = lambda **o: lib.lora_attn_prefill(*dict(base, **o).values())  # noqa: E731
     assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
