@@ -46,7 +46,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base,lrmulti")
+    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base,act,lrmulti")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -147,8 +147,18 @@ def decode_bytes(w):
     n_proj = int(w.has_k) + int(w.has_v)
     tok_groups = sum(w.segments[i].T for i in range(len(w.segments)))
     base = tok_groups * w.Hkv * w.d * es * 2
-    lr = sum(w.segments[i].T * sum(w.pool_rank[p] for p in w.segments[i].pools)
-             for i in range(len(w.segments))) * es * n_proj
+    # low-rank rows from the earliest activation position among the sequences
+    # that read a (segment, pool) pair
+    first = {}
+    for sq in w.seqs:
+        if sq.agent < 0:
+            continue
+        off = 0
+        for sid in sq.segments:
+            key = (sid, w.pool_of_agent[sq.agent])
+            first[key] = min(first.get(key, 1 << 60), max(0, sq.adapter_start - off))
+            off += w.segments[sid].T
+    lr = sum(max(0, w.segments[sid].T - st) * w.pool_rank[p] for (sid, p), st in first.items()) * es * n_proj
     used_agents = sorted({sq.agent for sq in w.seqs if sq.agent >= 0})
     bmat = sum(w.ranks[a] * w.Hkv * w.d * es * n_proj for a in used_agents)
     qo = w.S * w.Hq * w.d * es * 2
@@ -165,9 +175,10 @@ def decode_flops(w):
         a = w.seqs[s].agent
         rk = w.ranks[a] if (a >= 0 and w.has_k) else 0
         rv = w.ranks[a] if (a >= 0 and w.has_v) else 0
-        f += 2 * T * rk * w.Hkv * w.d  # rebuild L_k B_k (per agent, per KV head)
+        Ta = max(0, T - max(0, w.seqs[s].adapter_start))  # tokens carrying adapter terms
+        f += 2 * Ta * rk * w.Hkv * w.d  # rebuild L_k B_k (per agent, per KV head)
         f += 2 * T * w.Hq * w.d * 2  # QK and PV
-        f += 2 * T * w.Hq * rv  # P L_v
+        f += 2 * Ta * w.Hq * rv  # P L_v
         f += 2 * w.Hq * rv * w.d  # C B_v
     return f
 
@@ -186,9 +197,9 @@ def _traffic(kernel_src, launches_per_step=1):
 
 
 # ------------------------------------------------------------------ legs
-def leg_decode(K, W, adapt="kv"):
+def leg_decode(K, W, adapt="kv", starts=None):
     """The 8B-shaped decode; ``adapt`` "v" drops the key adapter (b_k NULL),
-    "none" both adapters."""
+    "none" both adapters; ``starts`` sets the agents' activation positions."""
     from workloads import config_8b_decode
     from workloads.device import upload
 
@@ -196,6 +207,8 @@ def leg_decode(K, W, adapt="kv"):
 
     w = config_8b_decode()
     w.adapt = adapt
+    for i, st in enumerate(starts or ()):
+        w.seqs[i].adapter_start = st
     dw = upload(w)
     ncopy = _replicate(dw, 2 * MALL_BYTES)
     wsb = lra.lora_attn_decode_workspace_size(w.S, 1, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len, lra.LRA_BF16)
@@ -314,8 +327,9 @@ def leg_prefill(K, W):
                 tokens=sum(sq.q_len for sq in w.seqs), build_bytes=4 * 2 * (512 * 4096 * 2 + 4096 * 16 * 2 + 512 * 16 * 2))
 
 
-def leg_prefill_absent(K, W, adapt):
-    """The prefill chunk's attention alone with absent adapters."""
+def leg_prefill_absent(K, W, adapt, starts=None):
+    """The prefill chunk's attention alone with absent adapters or
+    activation positions."""
     from workloads import config_prefill
     from workloads.device import upload
 
@@ -323,6 +337,8 @@ def leg_prefill_absent(K, W, adapt):
 
     w = config_prefill()
     w.adapt = adapt
+    for i, st in enumerate(starts or ()):
+        w.seqs[i].adapter_start = st
     dw = upload(w)
     out = dw.new_out()
 
@@ -385,9 +401,11 @@ def prefill_flops(w):
         rk = w.ranks[sq.agent] if (sq.agent >= 0 and w.has_k) else 0
         rv = w.ranks[sq.agent] if (sq.agent >= 0 and w.has_v) else 0
         nq = sq.q_len
+        st = max(0, sq.adapter_start)
         pairs = sum(T - nq + i + 1 for i in range(nq))
-        f += pairs * w.Hq * (2 * w.d * 2 + 2 * rv)
-        f += 2 * T * rk * w.Hkv * w.d
+        pairs_ad = sum(max(0, T - nq + i + 1 - st) for i in range(nq))  # visible pairs with an adapted key
+        f += pairs * w.Hq * 2 * w.d * 2 + pairs_ad * w.Hq * 2 * rv
+        f += 2 * max(0, T - st) * rk * w.Hkv * w.d
         f += 2 * nq * w.Hq * rv * w.d
     return f
 
@@ -526,6 +544,24 @@ def main():
                 "prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
                 "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": p["flops"]}
         log(f"{leg} legs done")
+    if "act" in legs:
+        # activated adapters: the 8B decode with the agents invoked for the
+        # last 512 tokens, and the prefill chunk with each agent activated at
+        # its own 512 new tokens (the shared prefix keeps the base cache)
+        d = leg_decode(K, W, "kv", starts=[8192 - 512] * 4)
+        gbs = d["bytes"] / (d["kernel_ms"] / 1e3) / 1e9
+        extra["decode_activated_last_512"] = {
+            "tokens_per_s": round(d["tokens"] / (d["step_ms"] / 1e3), 1),
+            "us_per_launch": round(d["kernel_ms"] * 1e3, 2), "GBps": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes_per_launch": d["bytes"]}
+        if "prefill" in legs:
+            p = leg_prefill_absent(K, W, "kv", starts=[8192] * 4)
+            tf = p["flops"] / (p["prefill_ms"] / 1e3) / 1e12
+            extra["prefill_activated_at_chunk"] = {
+                "prefill_tokens_per_s": round(p["tokens"] / (p["prefill_ms"] / 1e3), 1),
+                "prefill_ms": round(p["prefill_ms"], 4), "tflops": round(tf, 2),
+                "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4), "algorithmic_flops": p["flops"]}
+        log("activation legs done")
     if "lrmulti" in legs:
         lm = leg_lr_multi(K, W)
         gbs = lm["bytes"] / (lm["ms_multi"] / 1e3) / 1e9

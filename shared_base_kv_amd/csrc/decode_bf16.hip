@@ -131,9 +131,11 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, Wo
 // (a tile with fewer runs with zero B_k / L rows for the missing ones).
 // KAD / VAD: the call has key / value adapters; without one, that part of
 // the work (its low-rank loads, staging and products) is not compiled in.
+// ACT: the call passes activation positions (without them no position test
+// is compiled in).
 // Writes the split's record (m, l, seq, nact, O' per row), or the finished
 // rows when the context fits one split.
-template <int RP, int NA, bool KAD, bool VAD>
+template <int RP, int NA, bool KAD, bool VAD, bool ACT>
 __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const DecodeArgs a) {
   constexpr int NRT = RP / 16;
   constexpr int KC = RP >= 32 ? RP / 32 : 1;
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   auto load_lv = [&](Blk<RP>& B, int bi, const uint16_t* lk0, const uint16_t* lv0, int r0, int st_lo)
                      __attribute__((always_inline)) {
     const bool ok = bi < nb;
-    const bool lok = ok && (t_begin + bi * kBlock + kBlock > st_lo);
+    const bool lok = ok && (!ACT || t_begin + bi * kBlock + kBlock > st_lo);
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
     if constexpr (KAD) {
       const auto rlk = buf_rsrc(lk0 + (size_t)phys * kBlock * r0, lok ? kBlock * r0 * 2 : 0);
@@ -251,7 +253,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
         const int ag = sload(a.agent_ids + seq);
         t.seq = seq;
         if (ag >= 0) {
-          t.start = a.act ? sload(a.act + seq) : 0;
+          if constexpr (ACT) t.start = sload(a.act + seq);
           st_min = min(st_min, t.start);
           st_max = max(st_max, t.start);
           if constexpr (KAD) {
@@ -310,8 +312,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const uint16_t* lk0 = ADAPT ? uniform_ptr(s_agent[lead].lk) : nullptr;
   const uint16_t* lv0 = ADAPT ? uniform_ptr(s_agent[lead].lv) : nullptr;
   const int r0 = ADAPT ? uniform(s_agent[lead].r) : 0;
-  const int st_min = ADAPT ? uniform(s_start_min) : 0;  // blocks wholly before it skip the adapter work
-  const int st_max = ADAPT ? uniform(s_start_max) : 0;  // blocks from it on need no per-row mask
+  const int st_min = (ADAPT && ACT) ? uniform(s_start_min) : 0;  // blocks wholly before it skip the adapter work
+  const int st_max = (ADAPT && ACT) ? uniform(s_start_max) : 0;  // blocks from it on need no per-row mask
   load_lv(bufA, wave, lk0, lv0, r0, st_min);
 
   // ---- (5) staged values into LDS (waits for the first keys and the
@@ -358,7 +360,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const bool shared_l = s_shared_l != 0;
   const int row_al = lc / G;  // agent slot of this lane's query row
   const bool row_ok = row_al < ns && lc < a.apt * G;
-  const int row_start = (ADAPT && row_al < NA) ? s_agent[row_al].start : 0;  // this row's activation position
+  const int row_start = (ADAPT && ACT && row_al < NA) ? s_agent[row_al].start : 0;  // this row's activation position
   const uint16_t* qrow_p = s_q + lc * kQPitch;
   const uint16_t* qp_row = s_qp + lc * kQpPitch;
   const double rev_lane = KAD ? s_rev[lane] : 0.0;
@@ -386,7 +388,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // key rows (K) and value rows (V) separately
   auto load_agents = [&](AgentRows<RP, NA>& ar, int bi, bool keys, bool vals) __attribute__((always_inline)) {
     if (shared_l) return;  // every agent reads agent 0's rows, which travel with the block
-    const bool ok = bi < nb && (t_begin + bi * kBlock + kBlock > st_min);
+    const bool ok = bi < nb && (!ACT || t_begin + bi * kBlock + kBlock > st_min);
     const int phys = sload(bt_row + blk0 + (ok ? bi : 0));
 #pragma unroll
     for (int al = 1; al < NA; ++al) {
@@ -510,9 +512,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     // the adapter products; in a block that some row's position falls inside
     // or after, tokens before that row's position are masked out of its
     // adapter score and of its P L_v.
-    const bool blk_ad = tb + kBlock > st_min;
-    const bool blk_mask = tb < st_max;
-    const int on_from = row_start - tb - 4 * lg;  // token jj of this lane is on iff jj >= on_from
+    const bool blk_ad = !ACT || tb + kBlock > st_min;
+    // token jj of this lane carries adapter terms iff jj >= on_from (a block
+    // from every row's position on masks nothing: no branch either way)
+    const int on_from = (ACT && tb < st_max) ? row_start - tb - 4 * lg : -4;
     if constexpr (KAD) {
       if (blk_ad) {
         if (shared_l) {
@@ -533,7 +536,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 #pragma unroll
     for (int al = 1; al < NA; ++al)
       if (row_al == al) sad = sa[al];
-    if (KAD && blk_mask) {
+    if constexpr (KAD) {
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) sad[jj] = jj >= on_from ? sad[jj] : 0.f;
     }
@@ -577,12 +580,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb)
       o[cb] = mfma16(as_i16x4(make_uint2(B.vr[cb].x & m01, B.vr[cb].y & m23)), as_i16x4(pop), o[cb]);
-    // C^T += L_v^T P^T (per agent pool; rows of other agents masked out)
-    if (VAD && blk_ad) {
-      uint2 popc = pop;
-      if (blk_mask)
-        popc = make_uint2(pop.x & ((0 >= on_from ? 0xFFFFu : 0u) | (1 >= on_from ? 0xFFFF0000u : 0u)),
-                          pop.y & ((2 >= on_from ? 0xFFFFu : 0u) | (3 >= on_from ? 0xFFFF0000u : 0u)));
+    // C^T += L_v^T P^T (per agent pool; rows of other agents masked out).
+    // Blocks wholly before every activation position read zero L_v rows, so
+    // the products add exact zeros there.
+    if constexpr (VAD) {
+      const uint2 popc =
+          make_uint2(pop.x & ((0 >= on_from ? 0xFFFFu : 0u) | (1 >= on_from ? 0xFFFF0000u : 0u)),
+                     pop.y & ((2 >= on_from ? 0xFFFFu : 0u) | (3 >= on_from ? 0xFFFF0000u : 0u)));
       if (shared_l) {
 #pragma unroll
         for (int rr = 0; rr < NRT; ++rr)
@@ -807,7 +811,10 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
 
 template <int RP, int NA, bool KAD, bool VAD>
 void launch_main(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
-  hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  if (a.act)
+    hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD, true>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD, false>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
 }
 
 template <bool KAD, bool VAD>
@@ -831,6 +838,14 @@ bool launch_variant(const DecodeArgs& a, int rp, int na, dim3 grid, hipStream_t 
 
 }  // namespace
 
+// The variants with both adapters are built in a translation unit of their
+// own (this file compiled with LRA_DECODE_KV_PART), so the two halves of the
+// variant set compile in parallel.
+#ifdef LRA_DECODE_KV_PART
+bool launch_decode_bf16_kv(const DecodeArgs& a, int rp, int na, dim3 grid, hipStream_t stream) {
+  return launch_variant<true, true>(a, rp, na, grid, stream);
+}
+#else
 hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t stream) {
   const int per = (a.n_work + kNumXcd - 1) / kNumXcd;
   const dim3 grid(per * kNumXcd);
@@ -838,13 +853,13 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t s
   const bool kad = a.bk != nullptr, vad = a.bv != nullptr;
   bool launched;
   if (kad && vad)
-    launched = launch_variant<true, true>(a, rp, na, grid, stream);
+    launched = launch_decode_bf16_kv(a, rp, na, grid, stream);
   else if (vad)
     launched = launch_variant<false, true>(a, rp, na, grid, stream);
   else if (kad)
     launched = launch_variant<true, false>(a, rp, na, grid, stream);
   else {  // no adapter: one variant serves every tile width (no per-agent state)
-    launch_main<16, 1, false, false>(a, grid, stream);
+    hipLaunchKernelGGL((decode_bf16_kernel<16, 1, false, false, false>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
     launched = true;
   }
   if (!launched) return hipErrorInvalidValue;
@@ -853,5 +868,6 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t s
   hipLaunchKernelGGL(decode_bf16_combine, dim3(n_rows), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
+#endif
 
 }  // namespace lra

@@ -118,6 +118,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t stream);
+bool launch_decode_bf16_kv(const DecodeArgs& a, int rp, int na, dim3 grid, hipStream_t stream);
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_lr_build_bf16(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);

@@ -193,13 +193,16 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
       }
       if constexpr (KAD) {
         const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, lon * kBlock * r * 2);
+        // a key before the activation point reads no low-rank row (its
+        // rebuilt adapter term is then exactly zero)
+        const bool kon = key0 + lc >= a_start;
         if constexpr (RP == 16) {
-          const uint2 v = bld8(rlk, (4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
+          const uint2 v = bld8(rlk, (kon && 4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
           tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
         } else {
   #pragma unroll
           for (int kc = 0; kc < KC; ++kc)
-            tr.lk[kc] = bld16(rlk, (32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
+            tr.lk[kc] = bld16(rlk, (kon && 32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
         }
       }
       const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
@@ -219,12 +222,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     // ---- registers -> LDS: V^T, L_v^T as loaded; keys rebuilt as
     // K_base + rope(B_k^T L_k^T), rounded once to bf16. LAST marks the final
     // tile, the only one that can hold positions >= T (zeroed in V and L_v,
-    // whose products with P = 0 must stay finite). ----
+    // whose products with P = 0 must stay finite). Keys before the activation
+    // point got zero low-rank rows at load time, so their rebuilt key is the
+    // base key; their L_v columns are zeroed here. The rebuild itself has no
+    // branch, so it shares one basic block with the next tile's loads. ----
     auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
       constexpr bool LAST = decltype(last_tag)::value;
       const int key0 = t * kTile + kBlock * pw;
-      const bool blk_ad = key0 + kBlock > a_start;  // some key of the block carries adapter terms
-      const bool straddle = blk_ad && key0 < a_start;
+      const bool early = key0 < a_start;  // some key of the block is before the activation point
       uint16_t* sk = s_k[t & 1];
       uint16_t* sv = s_v[t % kVBufs];
       uint16_t* slv = s_lv[t % kVBufs];
@@ -245,7 +250,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         const int e = lane + 64 * u;
         if (e < 2 * RP) {
           uint4 v = tr.lvv[u];
-          if (LAST || straddle) {  // keys past the context or before the activation point
+          if (LAST || early) {  // keys past the context or before the activation point
             const int kk = key0 + 8 * (e & 1);
             uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
   #pragma unroll
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
           *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
         }
       }
-      if (!KAD || !blk_ad) {  // no key adapter on this block: the base keys as loaded
+      if constexpr (!KAD) {  // no key adapter: the base keys as loaded
   #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
           *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) = tr.kbl[cb];
@@ -266,10 +271,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         }
         return;
       }
-      if (straddle && key0 + lc < a_start) {  // this lane's key is before the activation point
-  #pragma unroll
-        for (int kc = 0; kc < (RP == 64 ? 2 : 1); ++kc) tr.lk[kc] = make_uint4(0, 0, 0, 0);
-      }
+
       const float* rot = s_rot[t & 1];
   #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
@@ -313,22 +315,22 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
             pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
       }
     };
-
+    auto store = [&](int t, auto last_tag) __attribute__((always_inline)) { store_tile(t, last_tag); };
 
     load_tile(0);
     if (n_tiles == 1)
-      store_tile(0, std::true_type{});
+      store(0, std::true_type{});
     else
-      store_tile(0, std::false_type{});
+      store(0, std::false_type{});
     if (n_tiles > 1) load_tile(1);
     __syncthreads();  // tile 0 is in LDS
     for (int kt = 0; kt < n_tiles; ++kt) {
       if (kt + 2 < n_tiles) {
-        store_tile(kt + 1, std::false_type{});
+        store(kt + 1, std::false_type{});
         load_tile(kt + 2);
         rot_table(kt + 2);
       } else if (kt + 1 < n_tiles) {
-        store_tile(kt + 1, std::true_type{});
+        store(kt + 1, std::true_type{});
       }
       __syncthreads();  // tile kt is consumed and tile kt + 1 is in LDS
     }
@@ -400,7 +402,6 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     }
 #pragma unroll
     for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
-      if (t * kTile + kTile <= a_start) break;  // tile wholly before the activation point
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
         const uint16_t* lr = slv + (16 * rr + lc) * kVPitch + 32 * kp + 4 * lg;
