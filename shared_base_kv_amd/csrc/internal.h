@@ -16,6 +16,7 @@ constexpr int kWaveBlocks = 2;   // cache blocks per wave in the smallest split
 constexpr int kMaxSplits = 64;   // split-K partitions per (group, head, row tile)
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxSplitBlocks = 256;  // cache blocks in one split (split <= 4096 tokens)
+constexpr int kPrefillRows = 256;     // query rows (tokens x query heads of one KV head) per prefill workgroup
 
 // Decode launch plan: derived on the host from sizes only, so the workspace
 // query and the launch agree.

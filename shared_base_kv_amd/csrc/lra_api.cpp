@@ -386,7 +386,7 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
   a.d = d;
   a.G = Hq / Hkv;
   a.max_q_len = max_q_len;
-  a.q_tiles = ceil_div(max_q_len, 128 / (Hq / Hkv));  // 128 query rows per workgroup
+  a.q_tiles = ceil_div(max_q_len, kPrefillRows / (Hq / Hkv));
   a.rp = pad_rank(max_rank);
   a.sm_scale = sm_scale;
   a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);

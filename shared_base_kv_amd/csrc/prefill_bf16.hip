@@ -14,27 +14,29 @@
 //     space, and C B_v is applied once per row after the key loop.
 //
 // Work decomposition: one workgroup = (sequence s, KV head h, query tile);
-// a query tile has 128 rows = 128/G query tokens x G query heads. The 8 waves
-// of a workgroup take two roles, one of each per SIMD: waves 0..3 consume
-// (32 query rows each: scores, softmax, P V on the matrix cores), waves 4..3+4
-// produce (each loads one 16-key cache block of the next tile and rebuilds its
-// keys on the vector units), so the rebuild of tile t+1 overlaps the matrix
-// work on tile t. All tiles of one KV head are dealt to one XCD, so the keys
-// they share (the common prefix) stream through one L2.
+// a query tile has 256 rows = 256/G query tokens x G query heads. Each of the
+// 8 waves (two per SIMD) consumes 32 query rows (scores, softmax, P V on the
+// matrix cores) and also produces part of the next tile: with a key adapter
+// every wave loads and rebuilds half of one 16-key cache block (half of the
+// rotary pairs and of the V^T rows), so the rebuild's registers fit beside
+// the consumer's; without one, waves 0..3 each copy a whole block. Two
+// consumers per SIMD let one wave's softmax, rebuild and LDS waits run under
+// the other's matrix work. All tiles of one KV head are dealt to one XCD, so
+// the keys they share (the common prefix) stream through one L2.
 //
 // Matrix-core mapping (16x16 tiles):
-//   X^T[dim, key]   = B_k^T L_k^T        (per wave: its 16-key block, 16x16x16 / 16x16x32)
+//   X^T[dim, key]   = B_k^T L_k^T        (per producer: its block's keys, 16x16x16 / 16x16x32)
 //   S^T[key, row]   = K_a Q^T            (16x16x32, K_a from LDS)
 //   O^T[dim, row]  += V^T P^T            (16x16x32, V^T from LDS, P^T from the S^T accumulators)
 //   C^T[rank, row] += L_v^T P^T
 //   O^T            += B_v^T C^T          (after the loop; C split into bf16 hi + lo)
 //
-// Pipeline (one barrier per tile): while the consumers work on tile t, the
-// producers rebuild tile t+1 into the other LDS buffers and the loads of tile
-// t+2 are in flight. Each consumer issues the scores of tile t and P V of tile
-// t-1 together and runs the softmax of tile t while the matrix cores work
-// through them; so keys are double-buffered in LDS and V^T, L_v^T
-// triple-buffered (tile t-1 is read while t+1 is written). The rotation of
+// Pipeline (one barrier per tile): in step t each wave issues the scores of
+// tile t and P V of tile t-1 together, runs the softmax of tile t while the
+// matrix cores work through them, then rebuilds its part of tile t+1 into
+// the other LDS buffers and issues the loads of tile t+2. Keys are
+// double-buffered in LDS and V^T, L_v^T triple-buffered (tile t-1 is read
+// while t+1 is written). The rotation of
 // the adapter key at position 64t + o is split by angle addition into a
 // per-tile part (64t, one table of 64 pairs per tile) and a per-lane part (o,
 // fixed for the whole loop), so no transcendental is evaluated per element.
@@ -47,13 +49,13 @@ namespace lra {
 namespace {
 
 constexpr int D = 128;
-constexpr int kRows = 128;     // query rows per workgroup
+constexpr int kRows = kPrefillRows;  // query rows per workgroup
 constexpr int kTile = 64;      // keys per tile (4 cache blocks)
 constexpr int kKPitch = D + 8;          // LDS row pitch of the key tile (bf16)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
 constexpr int kKBufs = 2;
 constexpr int kVBufs = 3;
-constexpr int kThreads = 512;  // 4 consumer + 4 producer waves
+constexpr int kThreads = 512;  // 8 waves of 32 query rows
 constexpr float kMaxSlack = 8.f;  // log2 of the largest probability kept before a rescale
 
 // (cos, sin) of one angle given in revolutions, with the revolution count
@@ -63,12 +65,17 @@ __device__ __forceinline__ float2 cos_sin_rev(double x) {
   return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
 }
 
-template <int RP>
-struct TileRegs {  // this wave's cache block of one tile, on its way from HBM
-  uint2 kbl[4], kbh[4];  // base keys, dims 16cb + 4lg .. +3 and +64, of key lc
-  uint4 vv[4];           // V^T rows 2 lane + u/2, keys 8 (u%2) .. +7 of the block
+// One producer wave's share of a 16-key cache block of a tile, on its way
+// from HBM: the whole block (NH = 1) or half of it (NH = 2: rotary pairs
+// 32 hh .. 32 hh + 31 and the V^T rows of parity hh).
+template <int RP, int NH>
+struct TileRegs {
+  static constexpr int NCB = 4 / NH;  // 16-pair groups cb
+  static constexpr int NPAR = 2 / NH; // V^T row parities
+  uint2 kbl[NCB], kbh[NCB];    // base keys of key lc: dims 16cb + 4lg .. +3 and +64
+  uint4 vv[NPAR][2];           // V^T row 2 lane + parity, keys 8k .. +7 of the block (k = 0, 1)
   uint4 lk[RP == 64 ? 2 : 1];  // L_k row of key lc: ranks 8lg.. (RP 32/64) or 4lg.. (RP 16, .x .y)
-  uint4 lvv[2];          // L_v^T items lane, lane + 64: rank item/2, keys 8 (item%2) .. +7
+  uint4 lvv[NPAR];             // L_v^T item lane + 64 u: rank item/2, keys 8 (item%2) .. +7
 };
 
 // KAD / VAD: the call has key / value adapters; without one, that part of
@@ -119,8 +126,13 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);
-  const bool producer = wave >= 4;  // waves 4..7: block `pw` of every tile
-  const int pw = wave & 3;
+  // Producers: with a key adapter every wave rebuilds half of block pw of
+  // each tile (the rebuild's registers then fit beside a consumer's);
+  // otherwise waves 0..3 each copy a whole block.
+  constexpr int NH = KAD ? 2 : 1;
+  const bool producer = NH == 2 || wave < 4;
+  const int pw = wave & 3;     // cache block of the tile this wave helps produce
+  const int hh = wave >> 2;    // its half (NH = 2)
   const int lc = lane & 15;
   const int lg = lane >> 4;
 
@@ -160,171 +172,182 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
 
   __syncthreads();  // B_k^T, B_v^T and the first rotary tables are in LDS
 
-  if (producer) {
-    // per-lane part (producers): key offset 16 pw + lc within the tile, pairs 16cb + 4lg + jj
-    float co[4][4], so[4][4];
-    if constexpr (KAD) {
-      const double off = (double)(kBlock * pw + lc);
-  #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-  #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const float2 cs = cos_sin_rev(off * s_rev[16 * cb + 4 * lg + jj]);
-          co[cb][jj] = cs.x;
-          so[cb][jj] = cs.y;
-        }
+  // per-lane part (producers): key offset 16 pw + lc within the tile, pairs 16cb + 4lg + jj
+  constexpr int NCB = 4 / NH, NPAR = 2 / NH;
+  const int cb0 = NH == 2 ? 2 * hh : 0;   // first 16-pair group of this wave
+  const int par0 = NH == 2 ? hh : 0;      // first V^T row parity / L_v^T item block of this wave
+  float co[NCB][4], so[NCB][4];
+  if constexpr (KAD) {
+    const double off = (double)(kBlock * pw + lc);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const float2 cs = cos_sin_rev(off * s_rev[16 * (cb0 + c) + 4 * lg + jj]);
+        co[c][jj] = cs.x;
+        so[c][jj] = cs.y;
+      }
+  }
+
+  // ---- global -> registers: block `pw` of tile t. Blocks past the
+  // visible keys get zero-length buffer ranges, so their loads return 0. ----
+  TileRegs<RP, NH> tr;
+  auto load_tile = [&](int t) __attribute__((always_inline)) {
+    const int key0 = t * kTile + kBlock * pw;
+    const bool valid = key0 < kv_end;
+    const int phys = uniform(bt_row[valid ? key0 / kBlock : 0]);
+    const int on = valid ? 1 : 0;
+    const int lon = (valid && key0 + kBlock > a_start) ? 1 : 0;  // low-rank rows needed
+    const auto rk = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
+                             on * kBlock * D * 2);
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int cb = cb0 + c;
+      tr.kbl[c] = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
+      tr.kbh[c] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
     }
+    if constexpr (KAD) {
+      const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, lon * kBlock * r * 2);
+      // a key before the activation point reads no low-rank row (its
+      // rebuilt adapter term is then exactly zero)
+      const bool kon = key0 + lc >= a_start;
+      if constexpr (RP == 16) {
+        const uint2 v = bld8(rlk, (kon && 4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
+        tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          tr.lk[kc] = bld16(rlk, (kon && 32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
+      }
+    }
+    const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
+                             on * D * kBlock * 2);
+#pragma unroll
+    for (int p = 0; p < NPAR; ++p)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) tr.vv[p][k] = bld16(rv, ((2 * lane + par0 + p) * kBlock + 8 * k) * 2);
+    if constexpr (VAD) {
+      const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, lon * r * kBlock * 2);
+#pragma unroll
+      for (int p = 0; p < NPAR; ++p) {
+        const int e = lane + 64 * (par0 + p), rank = e >> 1;
+        tr.lvv[p] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
+      }
+    }
+  };
 
-    // ---- global -> registers: block `pw` of tile t. Blocks past the
-    // visible keys get zero-length buffer ranges, so their loads return 0. ----
-    TileRegs<RP> tr;
-    auto load_tile = [&](int t) __attribute__((always_inline)) {
-      const int key0 = t * kTile + kBlock * pw;
-      const bool valid = key0 < kv_end;
-      const int phys = uniform(bt_row[valid ? key0 / kBlock : 0]);
-      const int on = valid ? 1 : 0;
-      const int lon = (valid && key0 + kBlock > a_start) ? 1 : 0;  // low-rank rows needed
-      const auto rk = buf_rsrc((const uint16_t*)a.kb + (size_t)phys * blk_elems + (size_t)h * kBlock * D,
-                               on * kBlock * D * 2);
-  #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        tr.kbl[cb] = bld8(rk, (lc * D + 16 * cb + 4 * lg) * 2);
-        tr.kbh[cb] = bld8(rk, (lc * D + 64 + 16 * cb + 4 * lg) * 2);
-      }
-      if constexpr (KAD) {
-        const auto rlk = buf_rsrc(lk + (size_t)phys * kBlock * r, lon * kBlock * r * 2);
-        // a key before the activation point reads no low-rank row (its
-        // rebuilt adapter term is then exactly zero)
-        const bool kon = key0 + lc >= a_start;
-        if constexpr (RP == 16) {
-          const uint2 v = bld8(rlk, (kon && 4 * lg < r) ? (lc * r + 4 * lg) * 2 : kOob);
-          tr.lk[0] = make_uint4(v.x, v.y, 0, 0);
-        } else {
-  #pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            tr.lk[kc] = bld16(rlk, (kon && 32 * kc + 8 * lg < r) ? (lc * r + 32 * kc + 8 * lg) * 2 : kOob);
-        }
-      }
-      const auto rv = buf_rsrc((const uint16_t*)a.vb + (size_t)phys * blk_elems + (size_t)h * D * kBlock,
-                               on * D * kBlock * 2);
-  #pragma unroll
-      for (int u = 0; u < 4; ++u) tr.vv[u] = bld16(rv, ((2 * lane + (u >> 1)) * kBlock + 8 * (u & 1)) * 2);
-      if constexpr (VAD) {
-        const auto rlv = buf_rsrc(lv + (size_t)phys * r * kBlock, lon * r * kBlock * 2);
-  #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const int e = lane + 64 * u, rank = e >> 1;
-          tr.lvv[u] = bld16(rlv, (e < 2 * RP && rank < r) ? (rank * kBlock + 8 * (e & 1)) * 2 : kOob);
-        }
-      }
-    };
-
-    // ---- registers -> LDS: V^T, L_v^T as loaded; keys rebuilt as
-    // K_base + rope(B_k^T L_k^T), rounded once to bf16. LAST marks the final
-    // tile, the only one that can hold positions >= T (zeroed in V and L_v,
-    // whose products with P = 0 must stay finite). Keys before the activation
-    // point got zero low-rank rows at load time, so their rebuilt key is the
-    // base key; their L_v columns are zeroed here. The rebuild itself has no
-    // branch, so it shares one basic block with the next tile's loads. ----
-    auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
-      constexpr bool LAST = decltype(last_tag)::value;
-      const int key0 = t * kTile + kBlock * pw;
-      const bool early = key0 < a_start;  // some key of the block is before the activation point
-      uint16_t* sk = s_k[t & 1];
-      uint16_t* sv = s_v[t % kVBufs];
-      uint16_t* slv = s_lv[t % kVBufs];
-  #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        uint4 v = tr.vv[u];
+  // ---- registers -> LDS: V^T, L_v^T as loaded; keys rebuilt as
+  // K_base + rope(B_k^T L_k^T), rounded once to bf16. LAST marks the final
+  // tile, the only one that can hold positions >= T (zeroed in V and L_v,
+  // whose products with P = 0 must stay finite). Keys before the activation
+  // point got zero low-rank rows at load time, so their rebuilt key is the
+  // base key; their L_v columns are zeroed here. The rebuild itself has no
+  // branch, so it shares one basic block with the next tile's loads. ----
+  auto store_tile = [&](int t, auto last_tag) __attribute__((always_inline)) {
+    constexpr bool LAST = decltype(last_tag)::value;
+    const int key0 = t * kTile + kBlock * pw;
+    const bool early = key0 < a_start;  // some key of the block is before the activation point
+    uint16_t* sk = s_k[t & 1];
+    uint16_t* sv = s_v[t % kVBufs];
+    uint16_t* slv = s_lv[t % kVBufs];
+#pragma unroll
+    for (int pp = 0; pp < NPAR; ++pp)
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        uint4 v = tr.vv[pp][k];
         if constexpr (LAST) {
-          const int kk = key0 + 8 * (u & 1);
+          const int kk = key0 + 8 * k;
           uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
-  #pragma unroll
+#pragma unroll
           for (int p = 0; p < 4; ++p)
             w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
         }
-        *reinterpret_cast<uint4*>(sv + (2 * lane + (u >> 1)) * kVPitch + kBlock * pw + 8 * (u & 1)) = v;
+        *reinterpret_cast<uint4*>(sv + (2 * lane + par0 + pp) * kVPitch + kBlock * pw + 8 * k) = v;
       }
-  #pragma unroll
-      for (int u = 0; u < (VAD ? 2 : 0); ++u) {
-        const int e = lane + 64 * u;
-        if (e < 2 * RP) {
-          uint4 v = tr.lvv[u];
-          if (LAST || early) {  // keys past the context or before the activation point
-            const int kk = key0 + 8 * (e & 1);
-            uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
-  #pragma unroll
-            for (int p = 0; p < 4; ++p) {
-              const int k1 = kk + 2 * p, k2 = k1 + 1;
-              w32[p] &= ((k1 >= a_start && (!LAST || k1 < T)) ? 0xFFFFu : 0u) |
-                        ((k2 >= a_start && (!LAST || k2 < T)) ? 0xFFFF0000u : 0u);
-            }
-          }
-          *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
-        }
-      }
-      if constexpr (!KAD) {  // no key adapter: the base keys as loaded
-  #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-          *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) = tr.kbl[cb];
-          *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) = tr.kbh[cb];
-        }
-        return;
-      }
-
-      const float* rot = s_rot[t & 1];
-  #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (RP == 16) {
-          const uint2 al_ = *reinterpret_cast<const uint2*>(s_bt + (16 * cb + lc) * RP + 4 * lg);
-          const uint2 ah_ = *reinterpret_cast<const uint2*>(s_bt + (16 * (cb + 4) + lc) * RP + 4 * lg);
-          const uint2 lk2 = make_uint2(tr.lk[0].x, tr.lk[0].y);
-          xl = mfma16(as_i16x4(al_), as_i16x4(lk2), xl);
-          xh = mfma16(as_i16x4(ah_), as_i16x4(lk2), xh);
-        } else {
-  #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            const uint4 al_ = *reinterpret_cast<const uint4*>(s_bt + (16 * cb + lc) * RP + 32 * kc + 8 * lg);
-            const uint4 ah_ = *reinterpret_cast<const uint4*>(s_bt + (16 * (cb + 4) + lc) * RP + 32 * kc + 8 * lg);
-            xl = mfma32(as_bf16x8(al_), as_bf16x8(tr.lk[kc]), xl);
-            xh = mfma32(as_bf16x8(ah_), as_bf16x8(tr.lk[kc]), xh);
+#pragma unroll
+    for (int pp = 0; pp < (VAD ? NPAR : 0); ++pp) {
+      const int e = lane + 64 * (par0 + pp);
+      if (e < 2 * RP) {
+        uint4 v = tr.lvv[pp];
+        if (LAST || early) {  // keys past the context or before the activation point
+          const int kk = key0 + 8 * (e & 1);
+          uint32_t* w32 = reinterpret_cast<uint32_t*>(&v);
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const int k1 = kk + 2 * p, k2 = k1 + 1;
+            w32[p] &= ((k1 >= a_start && (!LAST || k1 < T)) ? 0xFFFFu : 0u) |
+                      ((k2 >= a_start && (!LAST || k2 < T)) ? 0xFFFF0000u : 0u);
           }
         }
-        const float4 r01 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg));
-        const float4 r23 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg) + 4);
-        const float cB[4] = {r01.x, r01.z, r23.x, r23.z};
-        const float sB[4] = {r01.y, r01.w, r23.y, r23.w};
-        const float kl[4] = {__uint_as_float(tr.kbl[cb].x << 16), __uint_as_float(tr.kbl[cb].x & 0xFFFF0000u),
-                             __uint_as_float(tr.kbl[cb].y << 16), __uint_as_float(tr.kbl[cb].y & 0xFFFF0000u)};
-        const float kh[4] = {__uint_as_float(tr.kbh[cb].x << 16), __uint_as_float(tr.kbh[cb].x & 0xFFFF0000u),
-                             __uint_as_float(tr.kbh[cb].y << 16), __uint_as_float(tr.kbh[cb].y & 0xFFFF0000u)};
-        float y1[4], y2[4];
-  #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          // angle of pair 16cb + 4lg + jj at position 64t + 16 pw + lc
-          const float c = cB[jj] * co[cb][jj] - sB[jj] * so[cb][jj];
-          const float sn = sB[jj] * co[cb][jj] + cB[jj] * so[cb][jj];
-          const float u = xl[jj], w = xh[jj];
-          y1[jj] = __builtin_fmaf(-w, sn, __builtin_fmaf(u, c, kl[jj]));
-          y2[jj] = __builtin_fmaf(u, sn, __builtin_fmaf(w, c, kh[jj]));
-        }
-        *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) =
-            pack_bf16x4(y1[0], y1[1], y1[2], y1[3]);
-        *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) =
-            pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
+        *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
       }
-    };
-    auto store = [&](int t, auto last_tag) __attribute__((always_inline)) { store_tile(t, last_tag); };
+    }
+    if constexpr (!KAD) {  // no key adapter: the base keys as loaded
+#pragma unroll
+      for (int c = 0; c < NCB; ++c) {
+        const int cb = cb0 + c;
+        *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) = tr.kbl[c];
+        *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) = tr.kbh[c];
+      }
+      return;
+    }
 
+    const float* rot = s_rot[t & 1];
+#pragma unroll
+    for (int c = 0; c < NCB; ++c) {
+      const int cb = cb0 + c;
+      f32x4 xl = f32x4{0.f, 0.f, 0.f, 0.f}, xh = f32x4{0.f, 0.f, 0.f, 0.f};
+      if constexpr (RP == 16) {
+        const uint2 al_ = *reinterpret_cast<const uint2*>(s_bt + (16 * cb + lc) * RP + 4 * lg);
+        const uint2 ah_ = *reinterpret_cast<const uint2*>(s_bt + (16 * (cb + 4) + lc) * RP + 4 * lg);
+        const uint2 lk2 = make_uint2(tr.lk[0].x, tr.lk[0].y);
+        xl = mfma16(as_i16x4(al_), as_i16x4(lk2), xl);
+        xh = mfma16(as_i16x4(ah_), as_i16x4(lk2), xh);
+      } else {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const uint4 al_ = *reinterpret_cast<const uint4*>(s_bt + (16 * cb + lc) * RP + 32 * kc + 8 * lg);
+          const uint4 ah_ = *reinterpret_cast<const uint4*>(s_bt + (16 * (cb + 4) + lc) * RP + 32 * kc + 8 * lg);
+          xl = mfma32(as_bf16x8(al_), as_bf16x8(tr.lk[kc]), xl);
+          xh = mfma32(as_bf16x8(ah_), as_bf16x8(tr.lk[kc]), xh);
+        }
+      }
+      const float4 r01 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg));
+      const float4 r23 = *reinterpret_cast<const float4*>(rot + 2 * (16 * cb + 4 * lg) + 4);
+      const float cB[4] = {r01.x, r01.z, r23.x, r23.z};
+      const float sB[4] = {r01.y, r01.w, r23.y, r23.w};
+      const float kl[4] = {__uint_as_float(tr.kbl[c].x << 16), __uint_as_float(tr.kbl[c].x & 0xFFFF0000u),
+                           __uint_as_float(tr.kbl[c].y << 16), __uint_as_float(tr.kbl[c].y & 0xFFFF0000u)};
+      const float kh[4] = {__uint_as_float(tr.kbh[c].x << 16), __uint_as_float(tr.kbh[c].x & 0xFFFF0000u),
+                           __uint_as_float(tr.kbh[c].y << 16), __uint_as_float(tr.kbh[c].y & 0xFFFF0000u)};
+      float y1[4], y2[4];
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        // angle of pair 16cb + 4lg + jj at position 64t + 16 pw + lc
+        const float cs = cB[jj] * co[c][jj] - sB[jj] * so[c][jj];
+        const float sn = sB[jj] * co[c][jj] + cB[jj] * so[c][jj];
+        const float u = xl[jj], w = xh[jj];
+        y1[jj] = __builtin_fmaf(-w, sn, __builtin_fmaf(u, cs, kl[jj]));
+        y2[jj] = __builtin_fmaf(u, sn, __builtin_fmaf(w, cs, kh[jj]));
+      }
+      *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 16 * cb + 4 * lg) =
+          pack_bf16x4(y1[0], y1[1], y1[2], y1[3]);
+      *reinterpret_cast<uint2*>(sk + (kBlock * pw + lc) * kKPitch + 64 + 16 * cb + 4 * lg) =
+          pack_bf16x4(y2[0], y2[1], y2[2], y2[3]);
+    }
+  };
+  auto store = [&](int t, auto last_tag) __attribute__((always_inline)) { store_tile(t, last_tag); };
+
+  if (producer) {
     load_tile(0);
     if (n_tiles == 1)
       store(0, std::true_type{});
     else
       store(0, std::false_type{});
     if (n_tiles > 1) load_tile(1);
-    __syncthreads();  // tile 0 is in LDS
-    for (int kt = 0; kt < n_tiles; ++kt) {
+  }
+  auto produce = [&](int kt) __attribute__((always_inline)) {
+    if (producer) {
       if (kt + 2 < n_tiles) {
         store(kt + 1, std::false_type{});
         load_tile(kt + 2);
@@ -332,10 +355,8 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
       } else if (kt + 1 < n_tiles) {
         store(kt + 1, std::true_type{});
       }
-      __syncthreads();  // tile kt is consumed and tile kt + 1 is in LDS
     }
-    return;
-  }
+  };
 
   // ---- consumers ----
   // ---- query operands (consumers): this wave's rows 32w + 16rt + lc ----
@@ -346,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   for (int rt = 0; rt < 2; ++rt) {
     const int row = 32 * wave + 16 * rt + lc;
     const int t = row / G, j = row % G;
-    rok[rt] = !producer && (row < TQ * G) && (t < n_tok);
+    rok[rt] = (row < TQ * G) && (t < n_tok);
     rpos[rt] = p0 + t;
     const uint16_t* qp = (const uint16_t*)a.q + ((size_t)(q0 + t0 + t) * a.Hq + h * G + j) * D;
 #pragma unroll
@@ -484,18 +505,21 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     softmax(0, std::false_type{});
   else
     softmax(0, std::true_type{});
+  produce(0);
   __syncthreads();  // scores of tile 0 are done and tile 1 is in LDS
   int kt = 1;
   for (; kt < min(n_plain, n_tiles); ++kt) {
     scores(kt);
     pv(kt - 1);
     softmax(kt, std::false_type{});
+    produce(kt);
     __syncthreads();  // keys of tile kt and values of tile kt - 1 are consumed; tile kt + 1 is in LDS
   }
   for (; kt < n_tiles; ++kt) {
     scores(kt);
     pv(kt - 1);
     softmax(kt, std::true_type{});
+    produce(kt);
     __syncthreads();
   }
   pv(n_tiles - 1);
