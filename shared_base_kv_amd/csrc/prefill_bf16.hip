@@ -51,12 +51,19 @@ namespace {
 constexpr int D = 128;
 constexpr int kRows = kPrefillRows;  // query rows per workgroup
 constexpr int kTile = 64;      // keys per tile (4 cache blocks)
-constexpr int kKPitch = D + 8;          // LDS row pitch of the key tile (bf16)
+constexpr int kKPitch = D + 16;         // LDS row pitch of the key tile (bf16; 72 dwords: 16-byte reads conflict-free)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
 constexpr int kKBufs = 2;
 constexpr int kVBufs = 3;
 constexpr int kThreads = 512;  // 8 waves of 32 query rows
 constexpr float kMaxSlack = 8.f;  // log2 of the largest probability kept before a rescale
+
+// V^T and L_v^T tiles keep the 64 keys of a row in the order of the P^T
+// operand's k slots: lane group g reads keys 32kp + 4g .. +3 and 32kp + 16 +
+// 4g .. +3 as one 16-byte run at 32kp + 8g. kvpos(block, half) is where the
+// first of the 4-key runs of keys 8 half .. 8 half + 7 of cache block `block`
+// goes; the second run follows 8 halves later.
+__device__ __forceinline__ int kvpos(int block, int half) { return 32 * (block >> 1) + 16 * half + 4 * (block & 1); }
 
 // (cos, sin) of one angle given in revolutions, with the revolution count
 // reduced exactly in fp64 first.
@@ -262,7 +269,10 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
           for (int p = 0; p < 4; ++p)
             w32[p] &= (kk + 2 * p < T ? 0xFFFFu : 0u) | (kk + 2 * p + 1 < T ? 0xFFFF0000u : 0u);
         }
-        *reinterpret_cast<uint4*>(sv + (2 * lane + par0 + pp) * kVPitch + kBlock * pw + 8 * k) = v;
+        // keys 8k .. 8k + 7 of block pw land in the permuted key order (see kvpos)
+        uint16_t* row = sv + (2 * lane + par0 + pp) * kVPitch + kvpos(pw, k);
+        *reinterpret_cast<uint2*>(row) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2*>(row + 8) = make_uint2(v.z, v.w);
       }
 #pragma unroll
     for (int pp = 0; pp < (VAD ? NPAR : 0); ++pp) {
@@ -279,7 +289,9 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
                       ((k2 >= a_start && (!LAST || k2 < T)) ? 0xFFFF0000u : 0u);
           }
         }
-        *reinterpret_cast<uint4*>(slv + (e >> 1) * kVPitch + kBlock * pw + 8 * (e & 1)) = v;
+        uint16_t* row = slv + (e >> 1) * kVPitch + kvpos(pw, e & 1);
+        *reinterpret_cast<uint2*>(row) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2*>(row + 8) = make_uint2(v.z, v.w);
       }
     }
     if constexpr (!KAD) {  // no key adapter: the base keys as loaded
@@ -390,6 +402,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
   // ---- S^T[key, row] for the tile's 4 key blocks x this wave's 2 row tiles ----
   f32x4 sacc[4][2];
   auto scores = [&](int t) __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
     const uint16_t* sk = s_k[t & 1];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
@@ -404,6 +417,14 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
         for (int ks = 0; ks < 4; ++ks) sacc[kb][rt] = mfma32(kop[ks], qb[rt][ks], sacc[kb][rt]);
       }
     }
+    // key reads of two blocks ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
   // ---- O^T += V^T P^T ; C^T += L_v^T P^T for tile t with the P^T operands ----
@@ -415,8 +436,7 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     for (int db = 0; db < 8; ++db) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        const uint16_t* vr = sv + (16 * db + lc) * kVPitch + 32 * kp + 4 * lg;
-        const bf16x8 vop = cat8(*reinterpret_cast<const uint2*>(vr), *reinterpret_cast<const uint2*>(vr + kBlock));
+        const bf16x8 vop = as_bf16x8(*reinterpret_cast<const uint4*>(sv + (16 * db + lc) * kVPitch + 32 * kp + 8 * lg));
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) o[rt][db] = mfma32(vop, pop[rt][kp], o[rt][db]);
       }
@@ -425,12 +445,20 @@ __global__ __launch_bounds__(kThreads) void prefill_bf16_kernel(const PrefillArg
     for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
 #pragma unroll
       for (int kp = 0; kp < 2; ++kp) {
-        const uint16_t* lr = slv + (16 * rr + lc) * kVPitch + 32 * kp + 4 * lg;
-        const bf16x8 lop = cat8(*reinterpret_cast<const uint2*>(lr), *reinterpret_cast<const uint2*>(lr + kBlock));
+        const bf16x8 lop = as_bf16x8(*reinterpret_cast<const uint4*>(slv + (16 * rr + lc) * kVPitch + 32 * kp + 8 * lg));
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) cacc[rt][rr] = mfma32(lop, pop[rt][kp], cacc[rt][rr]);
       }
     }
+    // value reads three dim tiles ahead of the products that use them
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 1);
+    __builtin_amdgcn_sched_group_barrier(0x100, VAD ? 2 * NRT : 0, 1);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 12 + (VAD ? 4 * NRT : 0), 1);
   };
 
   // ---- online softmax (base 2) of tile t; MASK applies causality and the
