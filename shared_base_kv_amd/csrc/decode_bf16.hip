@@ -140,10 +140,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   constexpr int NRT = RP / 16;
   constexpr int KC = RP >= 32 ? RP / 32 : 1;
   constexpr int PW = D + (VAD ? RP : 0);  // floats per row of a merged state (O, then C)
+  // LDS row pitch of the merge buffer: an odd multiple of 8 floats, so the 16
+  // rows of a 16-byte access by one wave fall in distinct banks
+  constexpr int PWP = PW + 8;
+  static_assert((PWP / 8) % 2 == 1, "merge row pitch must be an odd multiple of 8 floats");
   constexpr int NT = kDecodeWaves * 64;
   constexpr int HW = kDecodeWaves / 2;
   constexpr int kBtBytes = KAD ? NA * D * RP * 2 : 0;
-  constexpr int kMergeBytes = HW * 16 * PW * 4;
+  constexpr int kMergeBytes = HW * 16 * PWP * 4;
   constexpr int kRegion = kBtBytes > kMergeBytes ? kBtBytes : kMergeBytes;
   static_assert(NA * RP <= 256, "staged B_k^T / B_v^T of a tile exceed their LDS budget");
   constexpr bool ADAPT = KAD || VAD;
@@ -227,13 +231,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     for (int cb = 0; cb < 8; ++cb) B.vr[cb] = bld8(rv, ((16 * cb + lc) * kBlock + 4 * lg) * 2);
   };
 
-  // ---- (1) the rotary table (kernel arguments), then the base keys of this
-  // wave's first block; later waits for the table cover nothing else ----
+  // ---- (1) loads that need no agent information: the rotary table (kernel
+  // arguments), the base keys of this wave's first block and the query
+  // tile. No branches around these loads (a load inside a conditional block
+  // gets a wait for every load in flight at the block's end); lanes without
+  // data read zero through the range check. ----
   double rev_arg = 0.0;
   if (KAD && tid < kMaxRopePairs) rev_arg = a.rope_rev[tid];
-  __builtin_amdgcn_sched_barrier(0);
   Blk<RP> bufA, bufB;
   load_k(bufA, wave);
+  const int qrow = tid / (D / 8), qd8 = (tid % (D / 8)) * 8;
+  const bool q_on = tid < 16 * (D / 8) && qrow / G < ns && qrow < a.apt * G;
+  const uint4 stq = bld16(buf_rsrc((const uint16_t*)a.q + ((size_t)s0 * a.Hq + h * G) * D, ns * a.Hq * D * 2),
+                          q_on ? (((qrow / G) * a.Hq + (qrow % G)) * D + qd8) * 2 : kOob);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- (2) agent table, from scalar loads only (which do not wait behind
@@ -243,36 +253,57 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // with an adapter; its low-rank rows travel with the blocks, and the
   // tile's pools count as shared when every adapted slot reads the lead's. ----
   if (ADAPT && wave == 0) {
+    // Two rounds of scalar loads in flight together (the agent ids, then every
+    // table entry of every slot); scheduling barriers keep all uses after all
+    // loads of a round. A slot past the tile or without an agent reads entry
+    // 0 (an adapter call has at least one agent) and is masked afterwards.
+    int ags[NA];
+#pragma unroll
+    for (int al = 0; al < NA; ++al) ags[al] = sload(a.agent_ids + s0 + min(al, ns - 1));
+    __builtin_amdgcn_sched_barrier(0);
+    const void* plk[NA];
+    const void* pbk[NA];
+    const void* plv[NA];
+    const void* pbv[NA];
+    int pr[NA], pst[NA];
+#pragma unroll
+    for (int al = 0; al < NA; ++al) {
+      const int idx = max(ags[al], 0);
+      plk[al] = KAD ? sload(a.lk + idx) : nullptr;
+      pbk[al] = KAD ? sload(a.bk + idx) : nullptr;
+      plv[al] = VAD ? sload(a.lv + idx) : nullptr;
+      pbv[al] = VAD ? sload(a.bv + idx) : nullptr;
+      pr[al] = sload(a.ranks + idx);
+      pst[al] = ACT ? sload(a.act + s0 + min(al, ns - 1)) : 0;
+    }
+    // every loaded value is used here, after the last load, so none of the
+    // loads moves into the branch of its slot below
+#pragma unroll
+    for (int al = 0; al < NA; ++al)
+      asm volatile("" ::"s"(plk[al]), "s"(pbk[al]), "s"(plv[al]), "s"(pbv[al]), "s"(pr[al]), "s"(pst[al]));
     int sh = 1, lead = -1, st_min = 0x7fffffff, st_max = 0;
     const uint16_t *lk0 = nullptr, *lv0 = nullptr;
     int r0 = 0;
+#pragma unroll
     for (int al = 0; al < NA; ++al) {
-      TileAgent t{nullptr, nullptr, nullptr, nullptr, 0, 0, 0};
-      if (al < ns) {
-        const int seq = s0 + al;
-        const int ag = sload(a.agent_ids + seq);
-        t.seq = seq;
-        if (ag >= 0) {
-          if constexpr (ACT) t.start = sload(a.act + seq);
-          st_min = min(st_min, t.start);
-          st_max = max(st_max, t.start);
-          if constexpr (KAD) {
-            t.lk = (const uint16_t*)sload(a.lk + ag);
-            t.bk = (const uint16_t*)sload(a.bk + ag);
-          }
-          if constexpr (VAD) {
-            t.lv = (const uint16_t*)sload(a.lv + ag);
-            t.bv = (const uint16_t*)sload(a.bv + ag);
-          }
-          t.r = sload(a.ranks + ag);
-          if (lead < 0) {
-            lead = al;
-            lk0 = t.lk;
-            lv0 = t.lv;
-            r0 = t.r;
-          } else {
-            sh &= (t.lk == lk0) & (t.lv == lv0) & (t.r == r0);
-          }
+      const bool adapted = al < ns && ags[al] >= 0;
+      TileAgent t{nullptr, nullptr, nullptr, nullptr, 0, s0 + al, 0};
+      if (adapted) {
+        t.lk = (const uint16_t*)plk[al];
+        t.bk = (const uint16_t*)pbk[al];
+        t.lv = (const uint16_t*)plv[al];
+        t.bv = (const uint16_t*)pbv[al];
+        t.r = pr[al];
+        t.start = pst[al];
+        st_min = min(st_min, t.start);
+        st_max = max(st_max, t.start);
+        if (lead < 0) {
+          lead = al;
+          lk0 = t.lk;
+          lv0 = t.lv;
+          r0 = t.r;
+        } else {
+          sh &= (t.lk == lk0) & (t.lv == lv0) & (t.r == r0);
         }
       }
       if (lane == 0) s_agent[al] = t;
@@ -287,25 +318,25 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   if (KAD && tid < kMaxRopePairs) s_rev[tid] = rev_arg;
   __syncthreads();
 
-  // ---- (3) staging loads: B_k, B_v rows of head h per agent, the query tile ----
+  // ---- (3) staging loads: B_k, B_v rows of head h per agent (branch-free,
+  // as in step 1) ----
   constexpr int kItemsB = ADAPT ? NA * RP * (D / 8) : 0;  // 8-dim chunks of B_k (and of B_v)
   constexpr int kPerB = ADAPT ? (kItemsB + NT - 1) / NT : 1;
+  static_assert(!ADAPT || (RP * (D / 8)) % 64 == 0, "one agent slot per wave and staging round");
   uint4 stk[kPerB], stv[kPerB];
 #pragma unroll
   for (int i = 0; i < kPerB; ++i) {
     const int e = tid + i * NT;
-    const int k = e % RP, d8 = ((e / RP) % (D / 8)) * 8, al = (e / (RP * (D / 8))) % NA;
+    const int k = e % RP, d8 = ((e / RP) % (D / 8)) * 8;
+    const int al = uniform((e / (RP * (D / 8))) % NA);  // the same for the whole wave
+    const int ra = e < kItemsB ? uniform(s_agent[al].r) : 0;
+    const int off = k < ra ? (k * HD + h * D + d8) * 2 : kOob;
     stk[i] = make_uint4(0, 0, 0, 0);
     stv[i] = make_uint4(0, 0, 0, 0);
-    if (e < kItemsB && k < s_agent[al].r) {
-      if constexpr (KAD) stk[i] = ld16(s_agent[al].bk + (size_t)k * HD + h * D + d8);
-      if constexpr (VAD) stv[i] = ld16(s_agent[al].bv + (size_t)k * HD + h * D + d8);
-    }
+    if constexpr (KAD) stk[i] = bld16(buf_rsrc(uniform_ptr(s_agent[al].bk), ra * HD * 2), off);
+    if constexpr (VAD) stv[i] = bld16(buf_rsrc(uniform_ptr(s_agent[al].bv), ra * HD * 2), off);
   }
-  uint4 stq = make_uint4(0, 0, 0, 0);
-  const int qrow = tid / (D / 8), qd8 = (tid % (D / 8)) * 8;
-  if (tid < 16 * (D / 8) && qrow / G < ns && qrow < a.apt * G)
-    stq = ld16((const uint16_t*)a.q + ((size_t)(s0 + qrow / G) * a.Hq + h * G + (qrow % G)) * D + qd8);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- (4) the rest of the first block ----
   const int lead = ADAPT ? uniform(s_lead) : 0;
@@ -316,8 +347,9 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   const int st_max = (ADAPT && ACT) ? uniform(s_start_max) : 0;  // blocks from it on need no per-row mask
   load_lv(bufA, wave, lk0, lv0, r0, st_min);
 
-  // ---- (5) staged values into LDS (waits for the first keys and the
-  // staging loads, not for the loads of step 4) ----
+  // ---- (5) staged values into LDS: waits for the staging loads and what
+  // was issued before them (the first block's keys), not for the loads of
+  // step 4 ----
   uint16_t* s_bt = reinterpret_cast<uint16_t*>(s_region);
 #pragma unroll
   for (int i = 0; i < kPerB; ++i) {
@@ -629,14 +661,14 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   // ---- merge the waves of this workgroup (two rounds through LDS) ----
   float l_row = wave_sum_across_groups(l_run);
   __syncthreads();  // B_k^T is dead from here on
-  float* obuf = reinterpret_cast<float*>(s_region);  // [HW][16][PW]
+  float* obuf = reinterpret_cast<float*>(s_region);  // [HW][16][PWP]
   if (wave >= HW) {
     const int slot = wave - HW;
     if (lg == 0) {
       s_ml[0][slot][lc] = m_run;
       s_ml[1][slot][lc] = l_row;
     }
-    float* ob = obuf + ((size_t)slot * 16 + lc) * PW;
+    float* ob = obuf + ((size_t)slot * 16 + lc) * PWP;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) *reinterpret_cast<f32x4*>(ob + 16 * cb + 4 * lg) = o[cb];
     if constexpr (VAD) {
@@ -650,7 +682,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     const float mm = fmaxf(m_run, m2);
     const float w1 = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - mm);
     const float w2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mm);
-    float* ob = obuf + ((size_t)wave * 16 + lc) * PW;
+    float* ob = obuf + ((size_t)wave * 16 + lc) * PWP;
 #pragma unroll
     for (int cb = 0; cb < 8; ++cb) {
       const f32x4 v = *reinterpret_cast<const f32x4*>(ob + 16 * cb + 4 * lg);
@@ -690,7 +722,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     f32x4 cm = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < HW; ++j)
-      cm += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + D + 16 * rr + 4 * lg);
+      cm += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PWP + D + 16 * rr + 4 * lg);
     float hi[4], lo[4];
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
@@ -709,7 +741,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
     f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < HW; ++j)
-      acc += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PW + 16 * cbt + 4 * lg);
+      acc += wts[j] * *reinterpret_cast<const f32x4*>(obuf + ((size_t)j * 16 + lc) * PWP + 16 * cbt + 4 * lg);
 #pragma unroll
     for (int rr = 0; rr < (VAD ? NRT : 0); ++rr) {
 #pragma unroll
