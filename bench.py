@@ -19,7 +19,9 @@ Other legs (same JSON line, under "legs"): the prefill chunk with its
 low-rank cache build, the 32-layer long-context decode, the 64-request
 serving mix, the tiny fp32 decode, the 8B decode and prefill chunk
 without a key adapter (b_k NULL) and without adapters, and the low-rank
-caches of 4 agents built from one segment's hidden states in one call. ``cpu_baseline``
+caches of 4 agents built from one segment's hidden states in one call, and one
+serving step (the 8B decode plus the prefill chunk) as one varlen launch
+against the two separate calls. ``cpu_baseline``
 times the fp64 oracle on the host on a bounded sample of the headline
 workload.
 """
@@ -46,7 +48,7 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base,act,lrmulti")
+    ap.add_argument("--legs", default="decode,prefill,long,mix,tiny,qv,base,act,lrmulti,varlen")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -352,6 +354,68 @@ def leg_prefill_absent(K, W, adapt, starts=None):
     return dict(prefill_ms=ms, flops=prefill_flops(w), tokens=sum(sq.q_len for sq in w.seqs))
 
 
+def leg_varlen(K, W):
+    """One serving step of the 8B-shaped layer (the 4-agent decode on its
+    8192-token base plus the 4 x 512-token prefill chunk): lora_attn_varlen
+    (one grid) against lora_attn_decode followed by lora_attn_prefill, with
+    the same context and query-length bounds."""
+    import torch
+
+    import shared_base_kv_amd as lra
+    from workloads import config_mixed_step
+    from workloads.device import upload
+
+    w = config_mixed_step()
+    dw = upload(w)
+    S_dec = 4
+    out = dw.new_out()
+    ng = dw.group_offsets.numel() - 1
+    wsv = torch.zeros(max(256, lra.lora_attn_varlen_workspace_size(w.S, S_dec, ng, w.Hq, w.Hkv, w.d, dw.max_rank,
+                                                                   dw.max_context_len, lra.LRA_BF16)),
+                      dtype=torch.uint8, device="cuda")
+    wsd = torch.zeros(max(256, lra.lora_attn_decode_workspace_size(S_dec, ng, w.Hq, w.Hkv, w.d, dw.max_rank,
+                                                                   dw.max_context_len, lra.LRA_BF16)),
+                      dtype=torch.uint8, device="cuda")
+    qd, qp = dw.q[:S_dec].contiguous(), dw.q[S_dec:].contiguous()
+    btd, btp = dw.block_tables[:S_dec].contiguous(), dw.block_tables[S_dec:].contiguous()
+    cd, cp = dw.context_lens[:S_dec].contiguous(), dw.context_lens[S_dec:].contiguous()
+    agd, agp = dw.agent_ids[:S_dec].contiguous(), dw.agent_ids[S_dec:].contiguous()
+    cup = (dw.cu_q_lens[S_dec:] - S_dec).contiguous()
+    od, op = out[:S_dec].clone(), out[S_dec:].clone()
+
+    def unified():
+        lra.lora_attn_varlen(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
+                             dw.cu_q_lens, dw.max_q_len, S_dec, dw.group_offsets, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs,
+                             dw.bk_ptrs, dw.bv_ptrs, dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta,
+                             out, wsv)
+
+    def separate():
+        lra.lora_attn_decode(qd, dw.k_base, dw.v_base, btd, cd, dw.max_context_len, dw.group_offsets, agd, dw.lk_ptrs,
+                             dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs, dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale,
+                             w.theta, od, wsd)
+        lra.lora_attn_prefill(qp, dw.k_base, dw.v_base, btp, cp, dw.max_context_len, cup, dw.max_q_len, agp,
+                              dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs, dw.ranks, dw.max_rank, w.n_agents, w.Hkv,
+                              w.sm_scale, w.theta, op)
+
+    def prefill_via_varlen():  # the prefill part alone through the varlen entry point
+        lra.lora_attn_varlen(qp, dw.k_base, dw.v_base, btp, cp, dw.max_context_len, cup, dw.max_q_len, 0, None, agp,
+                             dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs, dw.ranks, dw.max_rank, w.n_agents, w.Hkv,
+                             w.sm_scale, w.theta, op, None)
+
+    def prefill_alone():
+        lra.lora_attn_prefill(qp, dw.k_base, dw.v_base, btp, cp, dw.max_context_len, cup, dw.max_q_len, agp,
+                              dw.lk_ptrs, dw.lv_ptrs, dw.bk_ptrs, dw.bv_ptrs, dw.ranks, dw.max_rank, w.n_agents, w.Hkv,
+                              w.sm_scale, w.theta, op)
+
+    kk = max(4, K // 5)
+    t_uni = _timed(lambda i: unified(), kk, 2, 1)
+    t_sep = _timed(lambda i: separate(), kk, 2, 1)
+    t_pv = _timed(lambda i: prefill_via_varlen(), kk, 2, 1)
+    t_pa = _timed(lambda i: prefill_alone(), kk, 2, 1)
+    return dict(unified_ms=t_uni, separate_ms=t_sep, prefill_varlen_ms=t_pv, prefill_ms=t_pa,
+                tokens=int(dw.cu_q_lens[-1].item()), flops=prefill_flops(w), w=w)
+
+
 def leg_lr_multi(K, W, n_agents=4, rank=16):
     """Low-rank caches of every agent from one segment's hidden states: X
     [512, 4096] against the 2 * n_agents adapters' A (r=16 each) side by side,
@@ -570,6 +634,15 @@ def main():
             "us_per_adapter_calls": round(lm["ms_single"] * 1e3, 2), "GBps": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "algorithmic_bytes": lm["bytes"]}
         log("multi-adapter cache build leg done")
+    if "varlen" in legs:
+        vl = leg_varlen(K, W)
+        extra["varlen_serving_step"] = {
+            "tokens": vl["tokens"], "unified_ms": round(vl["unified_ms"], 4), "separate_ms": round(vl["separate_ms"], 4),
+            "tokens_per_s": round(vl["tokens"] / (vl["unified_ms"] / 1e3), 1),
+            "saved_us": round((vl["separate_ms"] - vl["unified_ms"]) * 1e3, 2),
+            "prefill_part_alone_ms": round(vl["prefill_ms"], 4),
+            "prefill_part_through_varlen_ms": round(vl["prefill_varlen_ms"], 4)}
+        log("varlen leg done")
     if "tiny" in legs:
         ti = leg_tiny(K, W)
         extra["tiny_f32"] = {"us_per_step": round(ti["step_ms"] * 1e3, 2), "kernel_us": round(ti["kernel_ms"] * 1e3, 2)}

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define LRA_VERSION 200
+#define LRA_VERSION 300
 
 typedef enum lra_status {
   LRA_OK = 0,
@@ -229,6 +229,44 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
                       const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
                       int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
                       int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Decode rows and prefill chunks in one launch (a serving step that mixes
+ * decoding sequences with prefill chunks: PReCache, Figure 1 caption, an
+ * agent's new segment prefilled while other agents decode; LRAgent: Efficient
+ * KV Cache Sharing for Multi-LoRA LLM Agents, abstract, concurrent agents on
+ * one shared base). Sequences 0 .. S_dec - 1 decode (one query each), the
+ * rest are prefill chunks. One grid runs both kinds of workgroups; each row's
+ * result is bit-identical to what lora_attn_decode (for the first S_dec
+ * sequences) and lora_attn_prefill (for the rest) would write.
+ *
+ *   q, out        [cu_q_lens[S], Hq, d]: decode sequence s < S_dec owns row s,
+ *                 prefill sequence s its rows cu_q_lens[s] .. cu_q_lens[s+1]-1.
+ *   cu_q_lens     int32 [S+1] with cu_q_lens[s] = s for s <= S_dec (not
+ *                 checked: it is device memory); may be NULL when S == S_dec.
+ *   max_q_len     (host) >= every prefill q_len_s (>= 1).
+ *   group_offsets int32 [num_groups+1] over the decode sequences only
+ *                 (0 .. S_dec), as for decode; NULL: each decode sequence its
+ *                 own group (num_groups ignored).
+ *   block_tables, context_lens, agent_ids, adapter_start: one entry (row) per
+ *                 sequence, decode sequences first.
+ *   Everything else as for decode and prefill. dtype: LRA_BF16, d = 128.
+ *   workspace     lora_attn_varlen_workspace_size(...) bytes (the decode
+ *                 part's split records), as for decode.
+ *   A call is one main kernel (decode and prefill workgroups), plus the
+ *   decode combine kernel when a decode context is split.
+ * ---------------------------------------------------------------------- */
+size_t lora_attn_varlen_workspace_size(int32_t S, int32_t S_dec, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
+                                       int32_t max_rank, int32_t max_context_len, int32_t dtype);
+
+int lora_attn_varlen(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                     int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len, const int32_t* cu_q_lens,
+                     int32_t max_q_len, int32_t S, int32_t S_dec, const int32_t* group_offsets, int32_t num_groups,
+                     const int32_t* agent_ids, const int32_t* adapter_start, const void* const* l_k_pools,
+                     const void* const* l_v_pools, const void* const* b_k, const void* const* b_v, const int32_t* ranks,
+                     int32_t max_rank, int32_t N_agents, int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                     float sm_scale, float rope_theta, int32_t dtype, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

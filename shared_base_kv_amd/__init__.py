@@ -15,6 +15,8 @@ from .binding import (  # noqa: F401
     lora_attn_decode_workspace_size,
     lora_attn_prefill,
     lora_attn_prefill_workspace_size,
+    lora_attn_varlen,
+    lora_attn_varlen_workspace_size,
     lr_cache_build,
     lr_cache_build_multi,
     lr_cache_build_workspace_size,

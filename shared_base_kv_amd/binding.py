@@ -34,6 +34,8 @@ EXPORTS = (
     "lora_attn_decode",
     "lora_attn_prefill_workspace_size",
     "lora_attn_prefill",
+    "lora_attn_varlen_workspace_size",
+    "lora_attn_varlen",
 )
 
 
@@ -79,6 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lora_attn_prefill_workspace_size.argtypes = size8
     lib.lora_attn_prefill.restype = ctypes.c_int
     lib.lora_attn_prefill.argtypes = attn
+    lib.lora_attn_varlen_workspace_size.restype = _sz
+    lib.lora_attn_varlen_workspace_size.argtypes = [_i32] * 9
+    lib.lora_attn_varlen.restype = ctypes.c_int
+    lib.lora_attn_varlen.argtypes = [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p,
+                                     _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _p, _p, _sz, _p]
     _lib = lib
     return lib
 
@@ -196,3 +203,25 @@ def lora_attn_prefill(q, k_base, v_base, block_tables, context_lens, max_context
         _ptr(l_v_pools),
         _ptr(b_k), _ptr(b_v), _ptr(ranks), max_rank, S, n_agents, Hq, Hkv, d, 16, sm_scale, rope_theta,
         _dtype_code(q), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def lora_attn_varlen_workspace_size(S, S_dec, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype) -> int:
+    return load().lora_attn_varlen_workspace_size(S, S_dec, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype)
+
+
+def lora_attn_varlen(q, k_base, v_base, block_tables, context_lens, max_context_len, cu_q_lens, max_q_len, S_dec,
+                     group_offsets, agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, n_agents, Hkv,
+                     sm_scale, rope_theta, out, workspace, stream=None, adapter_start=None):
+    """Decode rows (sequences 0 .. S_dec - 1, one query row each) and prefill
+    chunks (the rest) in one launch. q/out [cu_q_lens[S], Hq, d]; cu_q_lens
+    int32 [S+1] over all sequences (cu_q_lens[s] = s for s <= S_dec);
+    group_offsets over the decode sequences or None."""
+    _, Hq, d = q.shape
+    S = cu_q_lens.numel() - 1
+    num_groups = (group_offsets.numel() - 1) if group_offsets is not None else S_dec
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().lora_attn_varlen(
+        _ptr(q), _ptr(k_base), _ptr(v_base), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        max_context_len, _ptr(cu_q_lens), max_q_len, S, S_dec, _ptr(group_offsets), num_groups, _ptr(agent_ids),
+        _ptr(adapter_start), _ptr(l_k_pools), _ptr(l_v_pools), _ptr(b_k), _ptr(b_v), _ptr(ranks), max_rank, n_agents,
+        Hq, Hkv, d, 16, sm_scale, rope_theta, _dtype_code(q), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))

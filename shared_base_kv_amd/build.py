@@ -19,7 +19,8 @@ FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",
 ]
-SOURCES = ["lra_api.cpp", "decode_bf16.hip", "decode_bf16_kv.hip", "decode_f32.hip", "lr_build.hip", "prefill_bf16.hip"]
+SOURCES = ["lra_api.cpp", "decode_bf16.hip", "decode_bf16_kv.hip", "decode_f32.hip", "lr_build.hip", "prefill_bf16.hip",
+           "mixed_bf16.hip", "mixed_bf16_v.hip", "mixed_bf16_k.hip"]
 
 
 def _compile(src: str) -> str:

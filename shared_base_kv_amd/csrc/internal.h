@@ -123,5 +123,15 @@ bool launch_decode_bf16_kv(const DecodeArgs& a, int rp, int na, dim3 grid, hipSt
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_lr_build_bf16(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// prefill chunks (n_pre workgroups first) and decode rows in one grid, then
+// the decode combine when the decode part has split records
+hipError_t launch_varlen_bf16(const DecodeArgs& d, int rp, int na, const PrefillArgs& p, hipStream_t stream);
+bool launch_mixed_bf16_kv(const DecodeArgs& d, const PrefillArgs& p, int rp, int na, int n_pre, dim3 grid,
+                          hipStream_t stream);
+bool launch_mixed_bf16_v(const DecodeArgs& d, const PrefillArgs& p, int rp, int na, int n_pre, dim3 grid,
+                         hipStream_t stream);
+bool launch_mixed_bf16_k(const DecodeArgs& d, const PrefillArgs& p, int rp, int na, int n_pre, dim3 grid,
+                         hipStream_t stream);
+bool launch_mixed_bf16_none(const DecodeArgs& d, const PrefillArgs& p, int n_pre, dim3 grid, hipStream_t stream);
 
 }  // namespace lra

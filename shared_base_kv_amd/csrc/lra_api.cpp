@@ -180,6 +180,119 @@ int check_build_sizes(const char* name, int32_t n_tokens, int32_t hidden, int32_
   return LRA_OK;
 }
 
+// Validation and arguments of the decode kernels (sizes already checked,
+// S >= 1); shared by the decode call and the decode part of the varlen call.
+int make_decode_args(DecodeArgs& a, DecodePlan& p, const void* q, const void* k_base, const void* v_base,
+                     const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                     int32_t max_context_len, const int32_t* group_offsets, int32_t num_groups,
+                     const int32_t* agent_ids, const int32_t* adapter_start, const void* const* l_k_pools,
+                     const void* const* l_v_pools, const void* const* b_k, const void* const* b_v,
+                     const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents, int32_t Hq, int32_t Hkv,
+                     int32_t d, int32_t block_size, float sm_scale, float rope_theta, int32_t dtype, void* out,
+                     void* workspace, size_t workspace_bytes) {
+  if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
+    return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
+  if (!q || !k_base || !v_base || !block_tables || !context_lens || !out)
+    return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+  int rc = check_adapters(agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, N_agents);
+  if (rc != LRA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
+    return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
+  if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
+    return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
+  p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  const size_t need = p.partial_bytes;
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed (got %zu)", need, workspace_bytes);
+  a.q = q;
+  a.kb = k_base;
+  a.vb = v_base;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.group_offsets = group_offsets;
+  a.agent_ids = agent_ids;
+  a.act = (b_k || b_v) ? adapter_start : nullptr;
+  a.lk = l_k_pools;
+  a.lv = l_v_pools;
+  a.bk = b_k;
+  a.bv = b_v;
+  a.ranks = ranks;
+  a.out = out;
+  a.partials = need ? (float*)workspace : nullptr;
+  a.max_blocks = max_blocks;
+  a.num_groups = num_groups;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.G = p.G;
+  a.apt = p.apt;
+  a.row_tiles = p.row_tiles;
+  a.split = p.split;
+  a.nsplit = p.nsplit;
+  a.part_stride = p.part_stride;
+  a.n_work = num_groups * p.row_tiles * p.nsplit * Hkv;
+  a.sm_scale = sm_scale;
+  a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.rope = rope_theta > 0.f;
+  rope_table(a.rope_rev, rope_theta, d);
+  return LRA_OK;
+}
+
+// Validation and arguments of the prefill kernel (sizes already checked,
+// S >= 1, bf16); shared by the prefill call and the prefill part of the
+// varlen call.
+int make_prefill_args(PrefillArgs& a, const void* q, const void* k_base, const void* v_base,
+                      const int32_t* block_tables, int32_t max_blocks, const int32_t* context_lens,
+                      int32_t max_context_len, const int32_t* cu_q_lens, int32_t max_q_len, const int32_t* agent_ids,
+                      const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools,
+                      const void* const* b_k, const void* const* b_v, const int32_t* ranks, int32_t max_rank,
+                      int32_t S, int32_t N_agents, int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                      float sm_scale, float rope_theta, void* out) {
+  if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
+  if (max_q_len < 1 || max_q_len > max_context_len)
+    return fail(LRA_ERR_INVALID_ARG, "max_q_len must be in 1..max_context_len (got %d)", max_q_len);
+  if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
+    return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
+  if (!q || !k_base || !v_base || !block_tables || !context_lens || !cu_q_lens || !out)
+    return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+  int rc = check_adapters(agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, N_agents);
+  if (rc != LRA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
+    return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
+  if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
+    return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
+  a.q = q;
+  a.kb = k_base;
+  a.vb = v_base;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.cu_q_lens = cu_q_lens;
+  a.agent_ids = agent_ids;
+  a.act = (b_k || b_v) ? adapter_start : nullptr;
+  a.lk = l_k_pools;
+  a.lv = l_v_pools;
+  a.bk = b_k;
+  a.bv = b_v;
+  a.ranks = ranks;
+  a.out = out;
+  a.max_blocks = max_blocks;
+  a.S = S;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.G = Hq / Hkv;
+  a.max_q_len = max_q_len;
+  a.q_tiles = ceil_div(max_q_len, kPrefillRows / (Hq / Hkv));
+  a.rp = pad_rank(max_rank);
+  a.sm_scale = sm_scale;
+  a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
+  a.rope = rope_theta > 0.f;
+  rope_table(a.rope_rev, rope_theta, d);
+  return LRA_OK;
+}
+
 }  // namespace
 }  // namespace lra
 
@@ -276,55 +389,13 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
   int rc = check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
   if (rc != LRA_OK) return rc;
   if (S == 0) return ok();
-  if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
-  if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
-    return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
-  if (!q || !k_base || !v_base || !block_tables || !context_lens || !out)
-    return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
-  rc = check_adapters(agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, N_agents);
-  if (rc != LRA_OK) return rc;
-  if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
-    return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
-  if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
-    return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
-  const DecodePlan p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
-  const size_t need = p.partial_bytes;
-  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
-    return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed (got %zu)", need, workspace_bytes);
-
   DecodeArgs a{};
-  a.q = q;
-  a.kb = k_base;
-  a.vb = v_base;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.group_offsets = group_offsets;
-  a.agent_ids = agent_ids;
-  a.act = (b_k || b_v) ? adapter_start : nullptr;
-  a.lk = l_k_pools;
-  a.lv = l_v_pools;
-  a.bk = b_k;
-  a.bv = b_v;
-  a.ranks = ranks;
-  a.out = out;
-  a.partials = need ? (float*)workspace : nullptr;
-  a.max_blocks = max_blocks;
-  a.num_groups = num_groups;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.d = d;
-  a.G = p.G;
-  a.apt = p.apt;
-  a.row_tiles = p.row_tiles;
-  a.split = p.split;
-  a.nsplit = p.nsplit;
-  a.part_stride = p.part_stride;
-  a.n_work = num_groups * p.row_tiles * p.nsplit * Hkv;
-  a.sm_scale = sm_scale;
-  a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  a.rope = rope_theta > 0.f;
-  rope_table(a.rope_rev, rope_theta, d);
+  DecodePlan p{};
+  rc = make_decode_args(a, p, q, k_base, v_base, block_tables, max_blocks, context_lens, max_context_len,
+                        group_offsets, num_groups, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks,
+                        max_rank, S, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out, workspace,
+                        workspace_bytes);
+  if (rc != LRA_OK) return rc;
   const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
                                          : launch_decode_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
@@ -349,51 +420,72 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
   if (rc != LRA_OK) return rc;
   if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "prefill supports LRA_BF16 only");
   if (S == 0) return ok();
-  if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
-  if (max_q_len < 1 || max_q_len > max_context_len)
-    return fail(LRA_ERR_INVALID_ARG, "max_q_len must be in 1..max_context_len (got %d)", max_q_len);
-  if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
-    return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
-  if (!q || !k_base || !v_base || !block_tables || !context_lens || !cu_q_lens || !out)
-    return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
-  rc = check_adapters(agent_ids, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, N_agents);
-  if (rc != LRA_OK) return rc;
-  if (!aligned16(q) || !aligned16(k_base) || !aligned16(v_base) || !aligned16(out))
-    return fail(LRA_ERR_INVALID_ARG, "q, k_base, v_base and out must be 16-byte aligned");
-  if (!isfinite(sm_scale) || !isfinite(rope_theta) || rope_theta < 0.f)
-    return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
   (void)workspace;
   (void)workspace_bytes;
   PrefillArgs a{};
-  a.q = q;
-  a.kb = k_base;
-  a.vb = v_base;
-  a.block_tables = block_tables;
-  a.context_lens = context_lens;
-  a.cu_q_lens = cu_q_lens;
-  a.agent_ids = agent_ids;
-  a.act = (b_k || b_v) ? adapter_start : nullptr;
-  a.lk = l_k_pools;
-  a.lv = l_v_pools;
-  a.bk = b_k;
-  a.bv = b_v;
-  a.ranks = ranks;
-  a.out = out;
-  a.max_blocks = max_blocks;
-  a.S = S;
-  a.Hq = Hq;
-  a.Hkv = Hkv;
-  a.d = d;
-  a.G = Hq / Hkv;
-  a.max_q_len = max_q_len;
-  a.q_tiles = ceil_div(max_q_len, kPrefillRows / (Hq / Hkv));
-  a.rp = pad_rank(max_rank);
-  a.sm_scale = sm_scale;
-  a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
-  a.rope = rope_theta > 0.f;
-  rope_table(a.rope_rev, rope_theta, d);
+  rc = make_prefill_args(a, q, k_base, v_base, block_tables, max_blocks, context_lens, max_context_len, cu_q_lens,
+                         max_q_len, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, S,
+                         N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, out);
+  if (rc != LRA_OK) return rc;
   const hipError_t e = launch_prefill_bf16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_prefill launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+// --------------------------------------------------------------------------
+size_t lora_attn_varlen_workspace_size(int32_t S, int32_t S_dec, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
+                                       int32_t max_rank, int32_t max_context_len, int32_t dtype) {
+  if (S_dec < 0 || S_dec > S || dtype != LRA_BF16) return 0;
+  return lora_attn_decode_workspace_size(S_dec, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+}
+
+int lora_attn_varlen(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                     int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len, const int32_t* cu_q_lens,
+                     int32_t max_q_len, int32_t S, int32_t S_dec, const int32_t* group_offsets, int32_t num_groups,
+                     const int32_t* agent_ids, const int32_t* adapter_start, const void* const* l_k_pools,
+                     const void* const* l_v_pools, const void* const* b_k, const void* const* b_v, const int32_t* ranks,
+                     int32_t max_rank, int32_t N_agents, int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                     float sm_scale, float rope_theta, int32_t dtype, void* out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (S < 0 || S_dec < 0 || S_dec > S)
+    return fail(LRA_ERR_INVALID_ARG, "need 0 <= S_dec <= S (got S = %d, S_dec = %d)", S, S_dec);
+  if (!group_offsets) num_groups = S_dec;
+  int rc = check_decode_sizes(S, S_dec > 0 ? num_groups : 1, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  if (rc != LRA_OK) return rc;
+  if (dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "lora_attn_varlen supports LRA_BF16 only");
+  if (S_dec > 0 && (num_groups < 1 || num_groups > S_dec))
+    return fail(LRA_ERR_INVALID_ARG, "num_groups must be in 1..S_dec (got %d)", num_groups);
+  if (S == 0) return ok();
+  const int S_pre = S - S_dec;
+  DecodeArgs da{};
+  DecodePlan dp{};
+  if (S_dec > 0) {
+    rc = make_decode_args(da, dp, q, k_base, v_base, block_tables, max_blocks, context_lens, max_context_len,
+                          group_offsets, num_groups, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks,
+                          max_rank, S_dec, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out,
+                          workspace, workspace_bytes);
+    if (rc != LRA_OK) return rc;
+  } else {
+    dp.rp = pad_rank(max_rank);
+    dp.na = 1;
+    da.bk = b_k;
+    da.bv = b_v;
+  }
+  PrefillArgs pa{};
+  if (S_pre > 0) {
+    // the prefill part: sequences S_dec .. S - 1 (their per-sequence tables
+    // offset accordingly); cu_q_lens keeps absolute query row offsets
+    if (!block_tables || !context_lens || !cu_q_lens)
+      return fail(LRA_ERR_INVALID_ARG, "a required pointer argument is null");
+    rc = make_prefill_args(pa, q, k_base, v_base, block_tables + (size_t)S_dec * max_blocks, max_blocks,
+                           context_lens + S_dec, max_context_len, cu_q_lens + S_dec, max_q_len,
+                           agent_ids ? agent_ids + S_dec : nullptr, adapter_start ? adapter_start + S_dec : nullptr,
+                           l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, S_pre, N_agents, Hq, Hkv, d, block_size,
+                           sm_scale, rope_theta, out);
+    if (rc != LRA_OK) return rc;
+  }
+  const hipError_t e = launch_varlen_bf16(da, dp.rp, dp.na, pa, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_varlen launch failed: %s", hipGetErrorString(e));
   return ok();
 }
 

@@ -158,3 +158,30 @@ def test_multi_build_rejects_bad_group_tables():
     assert call(wsb=16) == B.LRA_ERR_WORKSPACE
     assert call(n=0) == B.LRA_OK
 
+
+
+def test_varlen_rejects_bad_arguments():
+    """The mixed decode + prefill call validates both parts before launching;
+    every case here fails (or is a no-op) on the host without touching memory."""
+    lib = lra.load()
+    base = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=600, ctx=FAKE, max_ctx=8704, cu=FAKE, mq=512, S=8,
+                S_dec=4, go=FAKE, ng=1, ag=FAKE, act=None, lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE,
+                max_rank=16, NA=4, Hq=32, Hkv=8, d=128, bs=16, sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE,
+                ws=FAKE, wsb=1 << 30, stream=None)
+    call = lambda **o: lib.lora_attn_varlen(*dict(base, **o).values())  # noqa: E731
+    assert call(S_dec=9) == B.LRA_ERR_INVALID_ARG
+    assert call(S_dec=-1) == B.LRA_ERR_INVALID_ARG
+    assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
+    assert call(ng=5) == B.LRA_ERR_INVALID_ARG  # more groups than decode sequences
+    assert call(cu=None) == B.LRA_ERR_INVALID_ARG  # prefill part without cu_q_lens
+    assert call(mq=0) == B.LRA_ERR_INVALID_ARG
+    assert call(wsb=100) == B.LRA_ERR_WORKSPACE  # the decode part's split records
+    assert call(q=FAKE + 2) == B.LRA_ERR_INVALID_ARG
+    assert call(bs=32) == B.LRA_ERR_UNSUPPORTED
+    assert call(bk=None, bv=None) == B.LRA_ERR_INVALID_ARG  # max_rank must be 0 without adapters
+    assert call(S=0, S_dec=0) == B.LRA_OK
+    f = lra.lora_attn_varlen_workspace_size
+    assert f(8, 4, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16) == lra.lora_attn_decode_workspace_size(
+        4, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16)
+    assert f(8, 0, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16) == 0  # prefill only: no split records
+    assert f(8, 9, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16) == 0

@@ -6,10 +6,12 @@ from .synth import (  # noqa: F401
     build_inputs,
     config_8b_decode,
     config_long_layer,
+    config_mixed_step,
     config_prefill,
     config_serving_mix,
     config_tiny_f32,
     decode_workload,
+    mixed_workload,
     prefill_workload,
     round_bf16,
 )

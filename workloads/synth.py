@@ -416,6 +416,76 @@ def config_prefill(seed=0):
     return prefill_workload(name="8b_prefill_chunk", seed=seed)
 
 
+def mixed_workload(
+    name="mixed",
+    dtype="bf16",
+    Hq=32,
+    Hkv=8,
+    d=128,
+    theta=5e5,
+    dec_group_sizes=(4,),
+    dec_context_lens=(1500,),
+    prefix=256,
+    q_lens=(100, 37, 300),
+    ranks=(16, 16, 16, 16),
+    shared_l=True,
+    dec_agents=None,
+    pre_agents=None,
+    shuffle=True,
+    seed=0,
+    adapt="kv",
+    adapter_starts=None,
+):
+    """Decode groups followed by prefill chunks over one set of paged pools
+    (the varlen call's batch). Decode sequences come first (one query each,
+    grouped: each group shares one base context); then one prefill chunk per
+    ``q_lens`` entry, all after one shared ``prefix``. Decode sequence i is
+    agent ``dec_agents[i]`` (default i mod the agent count), chunk j agent
+    ``pre_agents[j]`` (default j mod the agent count); -1: no adapter.
+    ``adapter_starts`` covers all sequences, decode ones first."""
+    n_agents = len(ranks)
+    S_dec = sum(dec_group_sizes)
+    dec_agents = [i % n_agents for i in range(S_dec)] if dec_agents is None else list(dec_agents)
+    pre_agents = [j % n_agents for j in range(len(q_lens))] if pre_agents is None else list(pre_agents)
+    if shared_l:
+        assert len(set(ranks)) == 1
+        pool_of_agent, pool_rank = [0] * n_agents, [ranks[0]]
+    else:
+        pool_of_agent, pool_rank = list(range(n_agents)), list(ranks)
+    pools_of = lambda ags: tuple(sorted({pool_of_agent[a] for a in ags if a >= 0}))  # noqa: E731
+    starts = [0] * (S_dec + len(q_lens)) if adapter_starts is None else [int(x) for x in adapter_starts]
+    segments, seqs, go = [], [], [0]
+    s = 0
+    for g, (gs, T) in enumerate(zip(dec_group_sizes, dec_context_lens)):
+        segments.append(Segment(T=T, pools=pools_of(dec_agents[s : s + gs])))
+        for i in range(gs):
+            seqs.append(SeqSpec(segments=(g,), agent=dec_agents[s + i], adapter_start=starts[s + i]))
+        s += gs
+        go.append(s)
+    pre = ()
+    if prefix:
+        assert prefix % BLOCK == 0
+        segments.append(Segment(T=prefix, pools=pools_of(pre_agents)))
+        pre = (len(segments) - 1,)
+    for j, ql in enumerate(q_lens):
+        segments.append(Segment(T=ql, pools=pools_of([pre_agents[j]])))
+        seqs.append(SeqSpec(segments=pre + (len(segments) - 1,), agent=pre_agents[j], q_len=ql,
+                            adapter_start=starts[S_dec + j]))
+    return Workload(
+        name=name, dtype=dtype, Hq=Hq, Hkv=Hkv, d=d, theta=theta, ranks=list(ranks),
+        pool_of_agent=pool_of_agent, pool_rank=pool_rank, segments=segments, seqs=seqs,
+        group_offsets=go if S_dec else None, seed=seed, shuffle=shuffle, adapt=adapt,
+    )
+
+
+def config_mixed_step(seed=0):
+    """One serving step of the 8B-shaped layer: the 4-agent decode on its
+    8192-token shared base plus the prefill chunk (4 agents x 512 new tokens
+    after an 8192-token shared prefix), shared-A r=16, bf16."""
+    return mixed_workload(name="8b_decode_plus_prefill_chunk", dec_group_sizes=(4,), dec_context_lens=(8192,),
+                          prefix=8192, q_lens=(512, 512, 512, 512), ranks=(16, 16, 16, 16), seed=seed)
+
+
 def build_inputs(n_tokens=512, hidden=4096, n_cols=16, seed=0, sigma_a=1.0 / 64):
     """X [n, hidden] ~ N(0,1) and A [hidden, n_cols] ~ N(0, sigma_a), bf16-rounded."""
     root = np.random.SeedSequence(seed)
