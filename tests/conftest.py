@@ -22,7 +22,7 @@ def _have_gpu() -> bool:
 
 
 def pytest_collection_modifyitems(config, items):
-    # Without any GPU (CPU container) GPU tests are skipped; on a GPU machine they
+    # Without a GPU the GPU tests are skipped; on a machine with a GPU they
     # run and fail loudly if the HIP library is missing.
     if _have_gpu():
         return
