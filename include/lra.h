@@ -28,7 +28,19 @@
  *   on the host before any HIP call; nothing throws or aborts. The message
  *   of the last failure on the calling thread is lra_last_error().
  * - Device-side contents (block ids, agent ids, lengths) are trusted: an
- *   out-of-range value is undefined behaviour.
+ *   out-of-range value is undefined behaviour. liblra_debug.so exports the
+ *   same entry points over the same kernels, built with LRA_DEBUG_CHECKS:
+ *   before each attention launch it checks on the device, for every
+ *   sequence, the context length (1..max_context_len), the block ids of the
+ *   used table entries (>= 0; the pool size is not passed, so not the upper
+ *   bound), the agent id (-1..N_agents-1), that agent's rank
+ *   (1..max_rank) and pool / B pointers, adapter_start (>= 0), the query
+ *   count (0..min(max_q_len, context length)), and that group_offsets rise
+ *   from 0 to S with every sequence of a group sharing the first one's
+ *   context length and block-table row. It synchronises `stream` to read
+ *   the verdict and returns LRA_ERR_INVALID_ARG naming the first failing
+ *   check before the attention kernels run (so it cannot be captured in a
+ *   graph).
  * - dtype applies to every floating-point tensor of a call (q, pools,
  *   adapters, out; X, A, L for the cache build). Accumulation is fp32.
  *

@@ -13,6 +13,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "liblra.so")
+# the same kernels with the device-side input checks (LRA_DEBUG_CHECKS)
+DEBUG_LIB_PATH = os.path.join(HERE, "liblra_debug.so")
 
 LRA_OK = 0
 LRA_ERR_INVALID_ARG = -1
@@ -54,9 +56,27 @@ _sz = ctypes.c_size_t
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """The library every wrapper below calls (loaded once)."""
     global _lib
-    if _lib is not None:
-        return _lib
+    if _lib is None:
+        _lib = _open(path)
+    return _lib
+
+
+_dlib = None
+
+
+def load_debug() -> ctypes.CDLL:
+    """liblra_debug.so, for direct C calls: each attention call first checks
+    the device-side inputs (and synchronises its stream). The wrappers below
+    keep using load()."""
+    global _dlib
+    if _dlib is None:
+        _dlib = _open(DEBUG_LIB_PATH)
+    return _dlib
+
+
+def _open(path: str) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise ImportError(f"{path} is not built; run python -m shared_base_kv_amd.build")
     lib = ctypes.CDLL(path)
@@ -86,7 +106,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.lora_attn_varlen.restype = ctypes.c_int
     lib.lora_attn_varlen.argtypes = [_p, _p, _p, _p, _i32, _p, _i32, _p, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p,
                                      _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _f32, _f32, _i32, _p, _p, _sz, _p]
-    _lib = lib
     return lib
 
 

@@ -23,9 +23,16 @@ SOURCES = ["lra_api.cpp", "decode_bf16.hip", "decode_bf16_kv.hip", "decode_f32.h
            "mixed_bf16.hip", "mixed_bf16_v.hip", "mixed_bf16_k.hip"]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+DEBUG_OUT = os.path.join(HERE, "liblra_debug.so")
+# the debug library: the same kernels, with the API layer built to check the
+# device-side inputs before each attention launch
+DEBUG_SOURCE = ("lra_api.cpp", "lra_api_debug", ["-DLRA_DEBUG_CHECKS"])
+
+
+def _compile(spec) -> str:
+    src, stem, extra = (spec, os.path.splitext(spec)[0], []) if isinstance(spec, str) else spec
+    obj = os.path.join(BUILD_DIR, stem + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
@@ -37,16 +44,18 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, OUT)
-    if verbose:
-        print(f"built {OUT}")
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        objs = list(ex.map(_compile, [*SOURCES, DEBUG_SOURCE]))
+    debug_obj = objs.pop()
+    for out, api_obj in ((OUT, objs[0]), (DEBUG_OUT, debug_obj)):
+        tmp = out + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", api_obj, *objs[1:], "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr}")
+        os.replace(tmp, out)
+        if verbose:
+            print(f"built {out}")
     return OUT
 
 

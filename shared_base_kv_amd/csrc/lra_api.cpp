@@ -108,6 +108,133 @@ int check_adapters(const int32_t* agent_ids, const void* const* l_k_pools, const
   return LRA_OK;
 }
 
+#ifdef LRA_DEBUG_CHECKS
+// Debug library only: the device-side data that the release library takes on
+// trust is checked on the device before each attention launch (the stream is
+// synchronised to read the verdict). The check kernel reads every table only
+// at indices it has bounded first, so bad data yields an error code, never an
+// access outside the caller's buffers.
+struct CheckArgs {
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  const int32_t* group_offsets;  // NULL: every sequence is its own group
+  const int32_t* cu_q_lens;      // NULL for decode
+  const int32_t* agent_ids;      // NULL without adapters
+  const int32_t* act;
+  const int32_t* ranks;
+  const void* const* lk;
+  const void* const* lv;
+  const void* const* bk;
+  const void* const* bv;
+  int32_t max_blocks, max_context_len, max_q_len, max_rank, S, num_groups, N_agents;
+};
+
+// in the order of report priority (per-sequence checks before group checks)
+enum : int {
+  kChkContext = 1,
+  kChkBlock,
+  kChkAgent,
+  kChkRank,
+  kChkPool,
+  kChkStart,
+  kChkQLen,
+  kChkGroups,
+  kChkGroupShare,
+};
+
+const char* check_message(int code) {
+  switch (code) {
+    case kChkContext: return "context length outside 1..max_context_len";
+    case kChkBlock: return "negative physical block id in a used block-table entry";
+    case kChkAgent: return "agent id outside -1..N_agents-1";
+    case kChkRank: return "agent rank outside 1..max_rank";
+    case kChkPool: return "null low-rank pool or B pointer for an agent in use";
+    case kChkStart: return "negative adapter_start";
+    case kChkGroups: return "group_offsets do not rise strictly from 0 to S";
+    case kChkGroupShare: return "sequences of one group differ in context length or block-table row";
+    case kChkQLen: return "query count outside 0..min(max_q_len, context length)";
+    default: return "unknown check";
+  }
+}
+
+// the failing check of lowest code, then lowest index, as code << 24 | index
+// (index: the sequence, or the group for the group checks); kNoFailure if none
+constexpr int kNoFailure = 0x7fffffff;
+__device__ int g_check;
+
+__device__ void report(int code, int idx) { atomicMin(&g_check, code << 24 | min(idx, 0xffffff)); }
+
+// one thread per sequence; thread s also checks group s
+__global__ void check_inputs_kernel(const CheckArgs c) {
+  const int s = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (s >= c.S) return;
+  const int T = c.context_lens[s];
+  if (T < 1 || T > c.max_context_len) return report(kChkContext, s);
+  const int nb = min((T + kBlock - 1) / kBlock, c.max_blocks);
+  for (int n = 0; n < nb; ++n)
+    if (c.block_tables[(size_t)s * c.max_blocks + n] < 0) return report(kChkBlock, s);
+  if (c.agent_ids) {
+    const int ag = c.agent_ids[s];
+    if (ag < -1 || ag >= c.N_agents) return report(kChkAgent, s);
+    if (ag >= 0) {
+      const int r = c.ranks[ag];
+      if (r < 1 || r > c.max_rank) return report(kChkRank, s);
+      if ((c.bk && (!c.bk[ag] || !c.lk[ag])) || (c.bv && (!c.bv[ag] || !c.lv[ag]))) return report(kChkPool, s);
+    }
+    if (c.act && c.act[s] < 0) return report(kChkStart, s);
+  }
+  if (c.cu_q_lens) {
+    const int ql = c.cu_q_lens[s + 1] - c.cu_q_lens[s];
+    if (ql < 0 || ql > c.max_q_len || ql > T) return report(kChkQLen, s);
+  }
+  if (c.group_offsets && s < c.num_groups) {
+    const int g0 = c.group_offsets[s], g1 = c.group_offsets[s + 1];
+    if (g0 < 0 || g1 <= g0 || g1 > c.S || (s == 0 && g0 != 0) || (s == c.num_groups - 1 && g1 != c.S))
+      return report(kChkGroups, s);
+    const int Tg = c.context_lens[g0];
+    const int nbg = min((Tg + kBlock - 1) / kBlock, c.max_blocks);
+    for (int i = g0 + 1; i < g1; ++i) {
+      if (c.context_lens[i] != Tg) return report(kChkGroupShare, s);
+      for (int n = 0; n < nbg; ++n)
+        if (c.block_tables[(size_t)i * c.max_blocks + n] != c.block_tables[(size_t)g0 * c.max_blocks + n])
+          return report(kChkGroupShare, s);
+    }
+  }
+}
+
+int debug_check(const CheckArgs& c, const char* name, hipStream_t stream) {
+  if (c.S < 1) return LRA_OK;
+  const int none = kNoFailure;
+  int got = kNoFailure;
+  hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_check), &none, sizeof(none), 0, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(check_inputs_kernel, dim3((c.S + 255) / 256), dim3(256), 0, stream, c);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbolAsync(&got, HIP_SYMBOL(g_check), sizeof(got), 0, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "%s: input check failed to run: %s", name, hipGetErrorString(e));
+  if (got != kNoFailure)
+    return fail(LRA_ERR_INVALID_ARG, "%s: %s (index %d)", name, check_message(got >> 24), got & 0xffffff);
+  return LRA_OK;
+}
+
+CheckArgs decode_check_args(const DecodeArgs& a, int max_context_len, int max_rank, int N_agents) {
+  const bool adapted = a.bk || a.bv;
+  return CheckArgs{a.block_tables, a.context_lens, a.group_offsets, nullptr, adapted ? a.agent_ids : nullptr,
+                   a.act, a.ranks, a.lk, a.lv, a.bk, a.bv, a.max_blocks, max_context_len, 0, max_rank, a.S,
+                   a.num_groups, N_agents};
+}
+
+CheckArgs prefill_check_args(const PrefillArgs& a, int max_context_len, int max_rank, int N_agents) {
+  const bool adapted = a.bk || a.bv;
+  return CheckArgs{a.block_tables, a.context_lens, nullptr, a.cu_q_lens, adapted ? a.agent_ids : nullptr,
+                   a.act, a.ranks, a.lk, a.lv, a.bk, a.bv, a.max_blocks, max_context_len, a.max_q_len, max_rank,
+                   a.S, a.S, N_agents};
+}
+#endif
+
 // Revolutions per position of rotary pair i: theta^(-2i/d) / (2 pi), in fp64.
 void rope_table(double* out, float theta, int d) {
   for (int i = 0; i < kMaxRopePairs; ++i)
@@ -396,6 +523,10 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
                         max_rank, S, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out, workspace,
                         workspace_bytes);
   if (rc != LRA_OK) return rc;
+#ifdef LRA_DEBUG_CHECKS
+  rc = debug_check(decode_check_args(a, max_context_len, max_rank, N_agents), "lora_attn_decode", (hipStream_t)stream);
+  if (rc != LRA_OK) return rc;
+#endif
   const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
                                          : launch_decode_f32(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
@@ -427,6 +558,10 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
                          max_q_len, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, S,
                          N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, out);
   if (rc != LRA_OK) return rc;
+#ifdef LRA_DEBUG_CHECKS
+  rc = debug_check(prefill_check_args(a, max_context_len, max_rank, N_agents), "lora_attn_prefill", (hipStream_t)stream);
+  if (rc != LRA_OK) return rc;
+#endif
   const hipError_t e = launch_prefill_bf16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_prefill launch failed: %s", hipGetErrorString(e));
   return ok();
@@ -484,6 +619,18 @@ int lora_attn_varlen(const void* q, const void* k_base, const void* v_base, cons
                            sm_scale, rope_theta, out);
     if (rc != LRA_OK) return rc;
   }
+#ifdef LRA_DEBUG_CHECKS
+  if (S_dec > 0) {
+    rc = debug_check(decode_check_args(da, max_context_len, max_rank, N_agents), "lora_attn_varlen (decode part)",
+                     (hipStream_t)stream);
+    if (rc != LRA_OK) return rc;
+  }
+  if (S_pre > 0) {
+    rc = debug_check(prefill_check_args(pa, max_context_len, max_rank, N_agents), "lora_attn_varlen (prefill part)",
+                     (hipStream_t)stream);
+    if (rc != LRA_OK) return rc;
+  }
+#endif
   const hipError_t e = launch_varlen_bf16(da, dp.rp, dp.na, pa, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_varlen launch failed: %s", hipGetErrorString(e));
   return ok();

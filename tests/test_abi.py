@@ -185,3 +185,23 @@ def test_varlen_rejects_bad_arguments():
         4, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16)
     assert f(8, 0, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16) == 0  # prefill only: no split records
     assert f(8, 9, 1, 32, 8, 128, 16, 8192, lra.LRA_BF16) == 0
+
+
+def test_debug_library_exports_and_validates_like_release():
+    """liblra_debug.so (the same kernels, device-side input checks) exports
+    every declared symbol and rejects bad host arguments exactly as liblra.so
+    does, before any HIP call."""
+    dbg = B.load_debug()
+    for n in _declared():
+        assert hasattr(dbg, n), n
+    assert dbg.lra_version() == lra.lra_version()
+    for over in (dict(q=None), dict(Hq=30), dict(d=64), dict(max_rank=65), dict(lk=None)):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=512, ctx=FAKE, max_ctx=8192, go=FAKE, ng=1, ag=FAKE,
+                    act=None, lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=16, S=4, NA=4, Hq=32, Hkv=8,
+                    d=128, bs=16, sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE, ws=FAKE, wsb=1 << 30,
+                    stream=None)
+        args.update(over)
+        rc_r = lra.load().lora_attn_decode(*args.values())
+        rc_d = dbg.lora_attn_decode(*args.values())
+        assert rc_r == rc_d != 0, over
+        assert lra.lra_last_error() == dbg.lra_last_error().decode(), over
