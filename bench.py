@@ -81,6 +81,56 @@ def _timed(launch, K, W, n_copies):
     return t0.elapsed_time(t1) / K
 
 
+def _per_launch_us(launch, n, n_copies):
+    """Per-launch times (us) of n back-to-back launches, each between two
+    events on the launch stream (so each includes its launch gap, as the mean
+    of _timed does): median, p10, p90."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int(2e6) + n * 200000)
+    for i in range(n):
+        ev[i].record()
+        launch(i % n_copies)
+    ev[n].record()
+    torch.cuda.synchronize()
+    d = sorted(ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(n))
+    q = lambda f: round(d[min(n - 1, int(round(f * (n - 1))))], 2)  # noqa: E731
+    return {"median": q(0.5), "p10": q(0.1), "p90": q(0.9), "launches": n,
+            "note": "each launch between two events of its own; the event records add about 2.5 us per launch, "
+                    "so ms_per_step (one event pair around all launches) is the throughput figure"}
+
+
+def hbm_measured():
+    """Measured HBM ceilings on this device, beside the published peak: a
+    4 GiB fp32 read (torch sum) and a 4 GiB copy (torch copy_), best of 5."""
+    import torch
+
+    n = 1 << 30
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    out = {}
+    for name, fn, nbytes in (("read_GBps", lambda: x.sum(), 4 * n), ("copy_GBps", lambda: y.copy_(x), 8 * n)):
+        fn()
+        best = None
+        for _ in range(5):
+            t0 = torch.cuda.Event(enable_timing=True)
+            t1 = torch.cuda.Event(enable_timing=True)
+            t0.record()
+            fn()
+            t1.record()
+            torch.cuda.synchronize()
+            ms = t0.elapsed_time(t1)
+            best = ms if best is None else min(best, ms)
+        out[name] = round(nbytes / (best / 1e3) / 1e9, 1)
+    del x, y
+    torch.cuda.empty_cache()
+    out["how"] = ("torch sum over 4 GiB fp32 (read) and copy_ of 4 GiB (read + write), best of 5; torch's own "
+                  "kernels, a lower bound on the attainable bandwidth; roofline.peak stays the published 8 TB/s")
+    return out
+
+
 def _p(t):
     """Device address of a tensor, 0 (NULL) for an absent one."""
     return 0 if t is None else t.data_ptr()
@@ -216,9 +266,10 @@ def leg_decode(K, W, adapt="kv", starts=None):
     wsb = lra.lora_attn_decode_workspace_size(w.S, 1, w.Hq, w.Hkv, w.d, dw.max_rank, dw.max_context_len, lra.LRA_BF16)
     launch, _, _, n = _decode_caller(dw, wsb)
     step_ms = _timed(launch, K, W, n)
+    per_launch = _per_launch_us(launch, max(K, 50), n)
     nbytes = decode_bytes(w)
     return dict(w=w, step_ms=step_ms, kernel_ms=step_ms, bytes=nbytes, flops=decode_flops(w), tokens=w.S,
-                copies=ncopy)
+                copies=ncopy, per_launch_us=per_launch)
 
 
 def leg_long(K, W):
@@ -484,9 +535,17 @@ def cpu_baseline(seconds):
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        threads = max([i.get("num_threads", 1) for i in blas] or [1])
+        vendor = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or "unknown"
     except Exception:
-        threads = 1
+        threads, vendor = 1, "unknown"
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), "unknown")
+    except OSError:
+        pass
     w = config_8b_decode()
     logical = [w.logical(s) for s in range(w.S)]
     done = 0
@@ -501,7 +560,8 @@ def cpu_baseline(seconds):
     return {"value": done / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle on the 8B-shaped decode workload: {done} sequence decodes "
                       f"({done // w.S} full 4-agent steps) in {dt:.1f} s, BLAS threads={threads}, "
-                      f"host cpus={len(os.sched_getaffinity(0))}"}
+                      f"host cpus={len(os.sched_getaffinity(0))}",
+            "cpu_model": model, "blas": vendor}
 
 
 def main():
@@ -557,7 +617,12 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "decode_bf16_kernel<16, 4, true, true, false> + decode_bf16_combine", "algorithmic_bytes_per_launch": head["bytes"],
                      "ms_per_launch": round(head["kernel_ms"], 5)},
+        "per_launch_us": head["per_launch_us"],
     }
+    try:
+        res["hbm_measured"] = hbm_measured()
+    except Exception as e:  # a measurement aid, never the product path
+        res["hbm_measured"] = {"error": str(e)[:200]}
     extra = {}
     if "prefill" in legs:
         try:
