@@ -235,15 +235,27 @@ def decode_flops(w):
     return f
 
 
-def _traffic(kernel_src, launches_per_step=1):
-    """HBM bytes per launch from the committed counter summary, or None if it
-    was taken on another version of the kernel source."""
+# every source the decode kernels are compiled from
+DECODE_SOURCES = ("decode_bf16.hip", "decode_bf16_kv.hip", "decode_bf16_body.h", "decode_bf16_body.inc",
+                  "device_common.h", "internal.h")
+
+
+def decode_source_sha256():
+    h = hashlib.sha256()
+    for name in DECODE_SOURCES:
+        h.update(name.encode())
+        h.update(open(os.path.join(ROOT, "shared_base_kv_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
+def _traffic():
+    """HBM bytes per decode call from the committed counter summary, or None
+    if the counters were taken on another version of the decode sources."""
     path = os.path.join(PROFILES, "decode_8b_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(os.path.join(ROOT, "shared_base_kv_amd", "csrc", kernel_src), "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != sha:
+    if rec.get("kernel_source_sha256") != decode_source_sha256():
         return None
     return rec.get("bytes_per_launch")
 
@@ -596,7 +608,7 @@ def main():
     step_s = head["step_ms"] / 1e3
     kern_s = head["kernel_ms"] / 1e3
     achieved = head["bytes"] / kern_s / 1e9
-    traffic = _traffic("decode_bf16.hip")
+    traffic = _traffic()
     res = {
         "metric": "LoRA-attn decode tokens/s (8B-shaped layer, 4 agents, shared base, T=8192)",
         "value": round(head["tokens"] / step_s, 1),

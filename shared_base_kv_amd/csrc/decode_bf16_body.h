@@ -108,7 +108,9 @@ struct WorkItem {
 // Logical work item -> (group, row tile, split, KV head). The KV head varies
 // fastest, so the heads of one split are consecutive items and share an XCD
 // (the low-rank rows of those tokens, shared by every head, reach that L2 once).
-__device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, WorkItem& w) {
+// First part: the group's sequences and the row tile's slots (false: the
+// tile has no sequences).
+__device__ __forceinline__ bool decode_item_rows(const DecodeArgs& a, int logical, WorkItem& w) {
   int rem = logical;
   w.h = rem % a.Hkv;
   rem /= a.Hkv;
@@ -121,12 +123,14 @@ __device__ __forceinline__ bool decode_item(const DecodeArgs& a, int logical, Wo
   w.s0 = w.s_first + w.rt * a.apt;
   w.ns = min(a.apt, s_end - w.s0);
   w.tile_id = (w.g * a.row_tiles + w.rt) * a.Hkv + w.h;
-  if (w.ns <= 0) return false;
+  return w.ns > 0;
+}
+// Second part: the group's context length and this split's token range.
+__device__ __forceinline__ void decode_item_span(const DecodeArgs& a, WorkItem& w) {
   w.T = sload(a.context_lens + w.s_first);
   w.nact = (w.T + a.split - 1) / a.split;
   w.t_begin = w.c * a.split;
   w.t_end = min(w.T, w.t_begin + a.split);
-  return true;
 }
 
 // Compile-time sizes of one workgroup's LDS.
