@@ -106,8 +106,8 @@ const char* lra_last_error(void);
  *   slot skips the row. Columns [0, n_cols) of each row are written.
  *   dtype: LRA_BF16. hidden % 8 == 0, 1 <= n_cols <= 512, ldx, lda >= their
  *   widths, X 16-byte aligned with ldx % 8 == 0.
- *   workspace: at least lr_cache_build_workspace_size(...) bytes of device
- *   memory (fp32 partial sums; contents on entry do not matter).
+ *   workspace: lr_cache_build_workspace_size(...) bytes, which is 0 (the sums
+ *   over hidden stay inside each workgroup); workspace may be NULL.
  * ---------------------------------------------------------------------- */
 size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_cols);
 

@@ -76,12 +76,10 @@ struct BuildArgs {
   const uint16_t* X;
   const uint16_t* A;
   const int64_t* slot_mapping;
-  float* partials;
   int64_t ldx, lda;
   int32_t n_tokens, hidden, n_cols;
-  int32_t ksplit, kchunk, row_tiles, col_tiles;
+  int32_t row_tiles, col_tiles;
   int32_t n_groups;
-  int32_t max_group_elems;  // max over groups of n_tokens * group width
   int32_t group_col[kMaxBuildGroups + 1];
   int32_t group_layout[kMaxBuildGroups];  // 0 token-major (row stride group_ld), 1 rank-major
   int64_t group_ld[kMaxBuildGroups];

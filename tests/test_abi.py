@@ -110,9 +110,8 @@ def test_build_rejects_bad_arguments():
     assert call(ncols=600, lda=600, ldl=600) == B.LRA_ERR_UNSUPPORTED
     assert call(lay=1) == B.LRA_ERR_INVALID_ARG  # rank-major needs a slot mapping
     assert call(ldl=8) == B.LRA_ERR_INVALID_ARG
-    assert call(wsb=10) == B.LRA_ERR_WORKSPACE
     assert call(n=0) == B.LRA_OK
-    assert lra.lr_cache_build_workspace_size(512, 4096, 16) == 8 * 512 * 16 * 4
+    assert lra.lr_cache_build_workspace_size(512, 4096, 16) == 0  # one launch, no partial sums
 
 
 def test_prefill_rejects_bad_arguments():
@@ -155,7 +154,6 @@ def test_multi_build_rejects_bad_group_tables():
     assert call(ng=0) == B.LRA_ERR_UNSUPPORTED
     assert call(ng=65) == B.LRA_ERR_UNSUPPORTED
     assert call(dtype=lra.LRA_F32) == B.LRA_ERR_UNSUPPORTED
-    assert call(wsb=16) == B.LRA_ERR_WORKSPACE
     assert call(n=0) == B.LRA_OK
 
 

@@ -36,9 +36,13 @@ def test_build_matches_oracle(shape):
     L = _build(X, A).float().cpu().numpy()
     ref = oracle.lr_cache_build(X, A)
     assert row_rel_err(L, ref) <= TOL_BF16
-    # diagnostic bound: one fp32 sum + one rounding keeps nearly all elements at RNE(fp64)
+    # diagnostic bound: one fp32 sum + one rounding keeps nearly all elements at
+    # RNE(fp64), except values on a bf16 rounding midpoint to within fp32
+    # precision, which the summation order decides either way
     rne = torch.from_numpy(ref).float().to(torch.bfloat16).float().numpy()
-    assert (L == rne).mean() >= 0.95
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    off_mid = np.abs(np.abs(ref - rne) - ulp / 2) > 1e-3 * ulp
+    assert (L == rne)[off_mid].mean() >= 0.95
 
 
 def test_build_paged_stores_bit_exact():
