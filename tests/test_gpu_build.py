@@ -29,7 +29,10 @@ def _build(X, A, **kw):
     return L
 
 
-@pytest.mark.parametrize("shape", [(512, 4096, 16), (512, 4096, 32), (1, 4096, 16), (37, 520, 8), (300, 2048, 200)])
+# hidden past 4096 takes several staging rounds (8200: three, the last 8 wide); 20 columns give
+# lda % 8 != 0 (the element-wise staging path); 40 columns end in a partial column tile
+@pytest.mark.parametrize("shape", [(512, 4096, 16), (512, 4096, 32), (1, 4096, 16), (37, 520, 8), (300, 2048, 200),
+                                   (70, 8200, 20), (33, 5000, 40)])
 def test_build_matches_oracle(shape):
     n, hidden, ncols = shape
     X, A = build_inputs(n, hidden, ncols, seed=n + ncols)
