@@ -38,7 +38,7 @@
  *   count (0..min(max_q_len, context length)), and that group_offsets rise
  *   from 0 to S with every sequence of a group sharing the first one's
  *   context length and block-table row. It synchronises `stream` to read
- *   the verdict and returns LRA_ERR_INVALID_ARG naming the first failing
+ *   the result and returns LRA_ERR_INVALID_ARG naming the first failing
  *   check before the attention kernels run (so it cannot be captured in a
  *   graph).
  * - dtype applies to every floating-point tensor of a call (q, pools,

@@ -111,7 +111,7 @@ int check_adapters(const int32_t* agent_ids, const void* const* l_k_pools, const
 #ifdef LRA_DEBUG_CHECKS
 // Debug library only: the device-side data that the release library takes on
 // trust is checked on the device before each attention launch (the stream is
-// synchronised to read the verdict). The check kernel reads every table only
+// synchronised to read the result). The check kernel reads every table only
 // at indices it has bounded first, so bad data yields an error code, never an
 // access outside the caller's buffers.
 struct CheckArgs {
