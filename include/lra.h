@@ -34,8 +34,10 @@
  *   sequence, the context length (1..max_context_len), the block ids of the
  *   used table entries (>= 0; the pool size is not passed, so not the upper
  *   bound), the agent id (-1..N_agents-1), that agent's rank
- *   (1..max_rank) and pool / B pointers, adapter_start (>= 0), the query
- *   count (0..min(max_q_len, context length)), and that group_offsets rise
+ *   (1..max_rank, a multiple of 8 with LRA_BF16) and pool / B pointers,
+ *   adapter_start (>= 0), the query count (0..min(max_q_len, context
+ *   length)), the decode rows of a varlen call (cu_q_lens[s] = s for
+ *   s <= S_dec), and that group_offsets rise
  *   from 0 to S with every sequence of a group sharing the first one's
  *   context length and block-table row. It synchronises `stream` to read
  *   the result and returns LRA_ERR_INVALID_ARG naming the first failing
@@ -254,8 +256,9 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
  *
  *   q, out        [cu_q_lens[S], Hq, d]: decode sequence s < S_dec owns row s,
  *                 prefill sequence s its rows cu_q_lens[s] .. cu_q_lens[s+1]-1.
- *   cu_q_lens     int32 [S+1] with cu_q_lens[s] = s for s <= S_dec (not
- *                 checked: it is device memory); may be NULL when S == S_dec.
+ *   cu_q_lens     int32 [S+1] with cu_q_lens[s] = s for s <= S_dec (device
+ *                 memory: trusted by liblra.so, checked by liblra_debug.so);
+ *                 may be NULL when S == S_dec.
  *   max_q_len     (host) >= every prefill q_len_s (>= 1).
  *   group_offsets int32 [num_groups+1] over the decode sequences only
  *                 (0 .. S_dec), as for decode; NULL: each decode sequence its

@@ -4,8 +4,6 @@ from .lra_oracle import (  # noqa: F401
     attend,
     kv_head_of,
     lora_attention,
-    lora_attn_decode,
-    lora_attn_prefill,
     lr_cache_build,
     lr_cache_build_multi,
     materialise_kv,

@@ -141,20 +141,6 @@ def lora_attention(q, kb, vb, lk, lv, bk, bv, *, sm_scale: float, theta: float, 
     return attend(np.asarray(q, np.float64), q_positions, K, V, sm_scale)
 
 
-def lora_attn_decode(seqs, *, sm_scale: float, theta: float) -> np.ndarray:
-    """Decode batch: ``seqs`` is a list of dicts (q [1,Hq,d], kb, vb, lk, lv,
-    bk, bv) per sequence; returns [S, Hq, d]."""
-    return np.concatenate(
-        [lora_attention(s["q"], s["kb"], s["vb"], s["lk"], s["lv"], s["bk"], s["bv"], sm_scale=sm_scale, theta=theta) for s in seqs]
-    )
-
-
-def lora_attn_prefill(seqs, *, sm_scale: float, theta: float) -> np.ndarray:
-    """Prefill batch: each dict's q [q_len, Hq, d] is appended causally at the
-    end of its context; returns the concatenated [sum q_len, Hq, d]."""
-    return lora_attn_decode(seqs, sm_scale=sm_scale, theta=theta)
-
-
 def lr_cache_build(X: np.ndarray, A: np.ndarray) -> np.ndarray:
     """Low-rank cache rows L = X A (fp64), X [n, hidden], A [hidden, r]."""
     return np.asarray(X, np.float64) @ np.asarray(A, np.float64)

@@ -119,6 +119,7 @@ struct CheckArgs {
   const int32_t* context_lens;
   const int32_t* group_offsets;  // NULL: every sequence is its own group
   const int32_t* cu_q_lens;      // NULL for decode
+  const int32_t* dec_cu_q_lens;  // varlen decode part: cu_q_lens[s] must be s for s <= S (else NULL)
   const int32_t* agent_ids;      // NULL without adapters
   const int32_t* act;
   const int32_t* ranks;
@@ -127,6 +128,7 @@ struct CheckArgs {
   const void* const* bk;
   const void* const* bv;
   int32_t max_blocks, max_context_len, max_q_len, max_rank, S, num_groups, N_agents;
+  int32_t dtype;  // LRA_BF16: ranks must be multiples of 8 (low-rank rows are read 16 bytes at a time)
 };
 
 // in the order of report priority (per-sequence checks before group checks)
@@ -138,6 +140,7 @@ enum : int {
   kChkPool,
   kChkStart,
   kChkQLen,
+  kChkDecodeRows,
   kChkGroups,
   kChkGroupShare,
 };
@@ -147,12 +150,13 @@ const char* check_message(int code) {
     case kChkContext: return "context length outside 1..max_context_len";
     case kChkBlock: return "negative physical block id in a used block-table entry";
     case kChkAgent: return "agent id outside -1..N_agents-1";
-    case kChkRank: return "agent rank outside 1..max_rank";
+    case kChkRank: return "agent rank outside 1..max_rank, or not a multiple of 8 with LRA_BF16";
     case kChkPool: return "null low-rank pool or B pointer for an agent in use";
     case kChkStart: return "negative adapter_start";
     case kChkGroups: return "group_offsets do not rise strictly from 0 to S";
     case kChkGroupShare: return "sequences of one group differ in context length or block-table row";
     case kChkQLen: return "query count outside 0..min(max_q_len, context length)";
+    case kChkDecodeRows: return "cu_q_lens[s] != s for a decode sequence s (or for s = S_dec)";
     default: return "unknown check";
   }
 }
@@ -178,7 +182,7 @@ __global__ void check_inputs_kernel(const CheckArgs c) {
     if (ag < -1 || ag >= c.N_agents) return report(kChkAgent, s);
     if (ag >= 0) {
       const int r = c.ranks[ag];
-      if (r < 1 || r > c.max_rank) return report(kChkRank, s);
+      if (r < 1 || r > c.max_rank || (c.dtype == LRA_BF16 && r % 8 != 0)) return report(kChkRank, s);
       if ((c.bk && (!c.bk[ag] || !c.lk[ag])) || (c.bv && (!c.bv[ag] || !c.lv[ag]))) return report(kChkPool, s);
     }
     if (c.act && c.act[s] < 0) return report(kChkStart, s);
@@ -187,6 +191,8 @@ __global__ void check_inputs_kernel(const CheckArgs c) {
     const int ql = c.cu_q_lens[s + 1] - c.cu_q_lens[s];
     if (ql < 0 || ql > c.max_q_len || ql > T) return report(kChkQLen, s);
   }
+  if (c.dec_cu_q_lens && (c.dec_cu_q_lens[s] != s || (s == c.S - 1 && c.dec_cu_q_lens[c.S] != c.S)))
+    return report(kChkDecodeRows, s);
   if (c.group_offsets && s < c.num_groups) {
     const int g0 = c.group_offsets[s], g1 = c.group_offsets[s + 1];
     if (g0 < 0 || g1 <= g0 || g1 > c.S || (s == 0 && g0 != 0) || (s == c.num_groups - 1 && g1 != c.S))
@@ -220,18 +226,19 @@ int debug_check(const CheckArgs& c, const char* name, hipStream_t stream) {
   return LRA_OK;
 }
 
-CheckArgs decode_check_args(const DecodeArgs& a, int max_context_len, int max_rank, int N_agents) {
+CheckArgs decode_check_args(const DecodeArgs& a, int max_context_len, int max_rank, int N_agents, int dtype,
+                            const int32_t* varlen_cu_q_lens = nullptr) {
   const bool adapted = a.bk || a.bv;
-  return CheckArgs{a.block_tables, a.context_lens, a.group_offsets, nullptr, adapted ? a.agent_ids : nullptr,
-                   a.act, a.ranks, a.lk, a.lv, a.bk, a.bv, a.max_blocks, max_context_len, 0, max_rank, a.S,
-                   a.num_groups, N_agents};
+  return CheckArgs{a.block_tables, a.context_lens, a.group_offsets, nullptr, varlen_cu_q_lens,
+                   adapted ? a.agent_ids : nullptr, a.act, a.ranks, a.lk, a.lv, a.bk, a.bv, a.max_blocks,
+                   max_context_len, 0, max_rank, a.S, a.num_groups, N_agents, dtype};
 }
 
 CheckArgs prefill_check_args(const PrefillArgs& a, int max_context_len, int max_rank, int N_agents) {
   const bool adapted = a.bk || a.bv;
-  return CheckArgs{a.block_tables, a.context_lens, nullptr, a.cu_q_lens, adapted ? a.agent_ids : nullptr,
+  return CheckArgs{a.block_tables, a.context_lens, nullptr, a.cu_q_lens, nullptr, adapted ? a.agent_ids : nullptr,
                    a.act, a.ranks, a.lk, a.lv, a.bk, a.bv, a.max_blocks, max_context_len, a.max_q_len, max_rank,
-                   a.S, a.S, N_agents};
+                   a.S, a.S, N_agents, LRA_BF16};
 }
 #endif
 
@@ -513,7 +520,8 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
                         workspace_bytes);
   if (rc != LRA_OK) return rc;
 #ifdef LRA_DEBUG_CHECKS
-  rc = debug_check(decode_check_args(a, max_context_len, max_rank, N_agents), "lora_attn_decode", (hipStream_t)stream);
+  rc = debug_check(decode_check_args(a, max_context_len, max_rank, N_agents, dtype), "lora_attn_decode",
+                   (hipStream_t)stream);
   if (rc != LRA_OK) return rc;
 #endif
   const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
@@ -610,8 +618,8 @@ int lora_attn_varlen(const void* q, const void* k_base, const void* v_base, cons
   }
 #ifdef LRA_DEBUG_CHECKS
   if (S_dec > 0) {
-    rc = debug_check(decode_check_args(da, max_context_len, max_rank, N_agents), "lora_attn_varlen (decode part)",
-                     (hipStream_t)stream);
+    rc = debug_check(decode_check_args(da, max_context_len, max_rank, N_agents, dtype, cu_q_lens),
+                     "lora_attn_varlen (decode part)", (hipStream_t)stream);
     if (rc != LRA_OK) return rc;
   }
   if (S_pre > 0) {

@@ -272,14 +272,98 @@ def _brute(q, kb, vb, lk, lv, bk, bv, sm_scale, theta):
 
 
 def pin_bruteforce_tiny(o):
-    """Vectorised oracle equals scalar loops on tiny inputs (T<=8, d=4, r<=2,
-    Hq=2, Hkv=1), with and without rotary, decode and causal prefill."""
+    """Vectorised oracle equals scalar loops on tiny inputs (T<=8, d=4, r<=2;
+    Hq=2 over one KV head, and Hq=4 over two KV heads, where B column h*d + i
+    must feed head h), with and without rotary, decode and causal prefill."""
     rng = np.random.default_rng(8)
-    for T, r, nq, theta in ((1, 1, 1, 0.0), (5, 2, 1, 1e4), (8, 2, 3, 5e5), (7, 1, 7, 10.0)):
-        c = _rand_case(rng, T=T, Hq=2, Hkv=1, d=4, r=r, nq=nq, scale_b=1.0)
+    for T, r, nq, theta, Hq, Hkv in ((1, 1, 1, 0.0, 2, 1), (5, 2, 1, 1e4, 2, 1), (8, 2, 3, 5e5, 2, 1),
+                                     (7, 1, 7, 10.0, 2, 1), (6, 2, 2, 1e4, 4, 2), (5, 2, 1, 0.0, 4, 2),
+                                     (4, 1, 4, 100.0, 2, 2)):
+        c = _rand_case(rng, T=T, Hq=Hq, Hkv=Hkv, d=4, r=r, nq=nq, scale_b=1.0)
         got = o.lora_attention(**c, sm_scale=0.6, theta=theta)
         ref = _brute(**c, sm_scale=0.6, theta=theta)
-        assert np.allclose(got, ref, atol=1e-12, rtol=0), (T, r, nq, theta, np.abs(got - ref).max())
+        assert np.allclose(got, ref, atol=1e-12, rtol=0), (T, r, nq, theta, Hkv, np.abs(got - ref).max())
+
+
+def _rot_complex(x, n, theta):
+    """Rotary embedding of the rows x [T, d] at positions n [T], written as a
+    complex product: pair (i, i + d/2) is the number x_i + j x_{i+d/2}, turned
+    by exp(j n theta^(-2i/d)). Independent of the oracle's rotate-half code."""
+    x = np.asarray(x, np.float64)
+    if theta == 0:
+        return x.copy()
+    h = x.shape[-1] // 2
+    z = x[:, :h] + 1j * x[:, h:]
+    w = np.exp(1j * np.outer(np.asarray(n, np.float64), np.power(float(theta), -np.arange(h) / h)))
+    zr = z * w
+    return np.concatenate([zr.real, zr.imag], axis=-1)
+
+
+def _reordered(c, sm_scale, theta, positions):
+    """Attention in the reordered form, never building full-dimension adapter
+    keys or values per head of the query: per query row j (KV head h) the
+    score splits as q.K_base[n] + q.rope_n(L_k[n] B_k), and the output as
+    P V_base + (P L_v) B_v, with the rank-space sum P L_v taken before B_v."""
+    q, kb, vb, lk, lv, bk, bv = (np.asarray(c[k], np.float64) for k in ("q", "kb", "vb", "lk", "lv", "bk", "bv"))
+    nq, Hq, d = q.shape
+    T, Hkv, _ = kb.shape
+    G = Hq // Hkv
+    out = np.zeros((nq, Hq, d))
+    for j in range(Hq):
+        h = j // G
+        bk_h, bv_h = bk[:, h * d:(h + 1) * d], bv[:, h * d:(h + 1) * d]
+        ad_key = _rot_complex(lk @ bk_h, np.arange(T), theta)  # [T, d]
+        for i in range(nq):
+            p = int(positions[i])
+            s = sm_scale * (kb[: p + 1, h] @ q[i, j] + ad_key[: p + 1] @ q[i, j])
+            e = np.exp(s - s.max())
+            P = e / e.sum()
+            out[i, j] = P @ vb[: p + 1, h] + (P @ lv[: p + 1]) @ bv_h
+    return out
+
+
+def pin_reorder_equals_materialised(o):
+    """The reordered form P V_base + (P L_v) B_v, with scores q.K_base +
+    q.rope(L_k B_k) (LRAgent abstract: attention reordered so the low-rank
+    cache is never expanded), equals attention over the materialised K, V, for
+    decode and causal prefill rows, GQA with two KV heads, rotary on and off."""
+    rng = np.random.default_rng(13)
+    for nq, theta, r in ((1, 0.0, 3), (1, 5e5, 2), (4, 1e4, 3), (2, 10.0, 1)):
+        c = _rand_case(rng, T=10, Hq=4, Hkv=2, d=8, r=r, nq=nq, scale_b=0.7)
+        pos = np.arange(10 - nq, 10)
+        ref = _reordered(c, 0.45, theta, pos)
+        K, V = o.materialise_kv(c["kb"], c["vb"], c["lk"], c["lv"], c["bk"], c["bv"], theta)
+        got = o.attend(np.asarray(c["q"], np.float64), pos, K, V, 0.45)
+        assert np.allclose(got, ref, atol=1e-12, rtol=0), (nq, theta, np.abs(got - ref).max())
+        full = o.lora_attention(**c, sm_scale=0.45, theta=theta)
+        assert np.allclose(full, ref, atol=1e-12, rtol=0), (nq, theta, np.abs(full - ref).max())
+
+
+def pin_shared_base_unchanged(o):
+    """Several agents over one base cache (LRAgent abstract: the base component
+    is shared; PReCache abstract): each agent's result over the shared base
+    arrays equals its result over a private copy of the base, exactly, in
+    either order of the agents, with one shared low-rank cache or one per
+    agent; the shared base arrays are left as they were."""
+    rng = np.random.default_rng(14)
+    T, Hq, Hkv, d, r = 11, 4, 2, 8, 3
+    kb = rng.standard_normal((T, Hkv, d))
+    vb = rng.standard_normal((T, Hkv, d))
+    kb0, vb0 = kb.copy(), vb.copy()
+    lk_sh, lv_sh = rng.standard_normal((T, r)), rng.standard_normal((T, r))
+    agents = []
+    for a in range(3):
+        own = a % 2 == 1
+        agents.append(dict(q=rng.standard_normal((2, Hq, d)),
+                           lk=rng.standard_normal((T, r)) if own else lk_sh,
+                           lv=rng.standard_normal((T, r)) if own else lv_sh,
+                           bk=0.5 * rng.standard_normal((r, Hkv * d)), bv=0.5 * rng.standard_normal((r, Hkv * d))))
+    private = [o.lora_attention(kb=kb0.copy(), vb=vb0.copy(), **ag, sm_scale=0.4, theta=1e4) for ag in agents]
+    for order in ((0, 1, 2), (2, 1, 0)):
+        for a in order:
+            got = o.lora_attention(kb=kb, vb=vb, **agents[a], sm_scale=0.4, theta=1e4)
+            assert np.array_equal(got, private[a]), (order, a)
+        assert np.array_equal(kb, kb0) and np.array_equal(vb, vb0), order
 
 
 # --------------------------------------------------------- cache-build pins

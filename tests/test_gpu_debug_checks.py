@@ -68,6 +68,7 @@ DECODE_CASES = {
     "agent_id": ("agent id", lambda dw: _set(dw.agent_ids, 1, 4)),
     "agent_below": ("agent id", lambda dw: _set(dw.agent_ids, 1, -2)),
     "rank": ("agent rank", lambda dw: _set(dw.ranks, 2, 17)),
+    "rank_not_multiple_of_8": ("agent rank", lambda dw: _set(dw.ranks, 2, 12)),
     "null_pool": ("null low-rank pool", lambda dw: _set(dw.lk_ptrs, 0, 0)),
     "group_offsets": ("group_offsets", lambda dw: _set(dw.group_offsets, 1, 0)),
     "group_context": ("differ in context length", lambda dw: _set(dw.context_lens, 1, 299)),
@@ -103,6 +104,21 @@ def test_bad_prefill_query_count_is_reported(use_debug):
     with pytest.raises(lra.LraError) as e:
         run_prefill(pw, out=out)
     assert e.value.code == B.LRA_ERR_INVALID_ARG and "query count" in str(e.value)
+    assert bool((out == SENTINEL).all())
+
+
+def test_varlen_decode_rows_are_checked(use_debug):
+    """Decode sequence s of a varlen call owns query row s: cu_q_lens[s] must
+    equal s up to s = S_dec (else prefill rows would overlap decode rows)."""
+    print("[case] debug library, varlen with a decode row offset moved", flush=True)
+    mw = upload(mixed_workload(name="dbgm", seed=9))
+    _set(mw.cu_q_lens, 2, 3)
+    use_debug()
+    out = torch.full(mw.q.shape, SENTINEL, dtype=mw.torch_dtype, device="cuda")
+    with pytest.raises(lra.LraError) as e:
+        run_varlen(mw, 4, out=out)
+    assert e.value.code == B.LRA_ERR_INVALID_ARG
+    assert "decode part" in str(e.value) and "cu_q_lens" in str(e.value), str(e.value)
     assert bool((out == SENTINEL).all())
 
 

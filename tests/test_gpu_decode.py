@@ -40,6 +40,8 @@ SMALL = [
     (32, 8, (2, 1, 3), (129, 16, 700), (16,) * 6, True, 1e4),
     (16, 8, (8,), (300,), (32,) * 8, False, 5e5),  # G=2, 8 agents/tile
     (8, 8, (5,), (77,), (8,) * 5, False, 5e5),  # G=1
+    (8, 8, (12,), (300,), (16,) * 12, False, 5e5),  # G=1, 12 agents in one tile (16-agent variant)
+    (32, 8, (3,), (400,), (16, 32, 8), False, 5e5),  # separate pools of different ranks in one tile
     (64, 8, (3,), (260,), (64,) * 3, False, 5e5),  # G=8: 2 agents per tile -> 2 row tiles
     (128, 8, (2,), (200,), (16, 16), False, 5e5),  # G=16: 1 agent per tile
     (32, 8, (6,), (513,), (64,) * 6, False, 5e5),  # 2 row tiles at r=64
@@ -57,8 +59,9 @@ def test_small_decode_variants(case):
 
 
 def test_tiny_f32_variants():
-    for theta, gs, tl in ((5e5, (3,), (100,)), (0.0, (1, 2), (16, 65)), (1e4, (2,), (1,))):
-        w = decode_workload(name="f32v", dtype="f32", Hq=8, Hkv=4, d=64, theta=theta, group_sizes=gs,
+    for theta, gs, tl, d in ((5e5, (3,), (100,), 64), (0.0, (1, 2), (16, 65), 64), (1e4, (2,), (1,), 64),
+                             (5e5, (2, 1), (130, 47), 128)):
+        w = decode_workload(name="f32v", dtype="f32", Hq=8, Hkv=4, d=d, theta=theta, group_sizes=gs,
                             context_lens=tl, ranks=(8,) * sum(gs), shared_l=False, seed=3)
         _check(w, TOL_F32)
 

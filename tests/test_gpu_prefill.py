@@ -50,7 +50,7 @@ SMALL = [
     (32, 8, 128, (64, 65, 3), 32, 5e5),
     (32, 8, 32, (70,), 64, 5e5),
     (32, 8, 48, (50, 9), 8, 5e5),
-    (8, 8, 32, (130,), 16, 5e5),    # G=1: 128 tokens per tile
+    (8, 8, 32, (300,), 16, 5e5),    # G=1: 256 tokens per tile, two tiles
     (16, 8, 16, (90,), 16, 5e5),    # G=2
     (64, 8, 16, (40,), 16, 5e5),    # G=8
     (128, 8, 16, (20,), 16, 5e5),   # G=16

@@ -21,12 +21,12 @@ def _n_groups(dw, S_dec):
     return dw.group_offsets.numel() - 1 if dw.group_offsets is not None else S_dec
 
 
-def run_varlen(dw, S_dec):
+def run_varlen(dw, S_dec, out=None):
     w = dw.w
     n = lra.lora_attn_varlen_workspace_size(w.S, S_dec, _n_groups(dw, S_dec), w.Hq, w.Hkv, w.d, dw.max_rank,
                                             dw.max_context_len, lra.LRA_BF16)
     ws = torch.zeros(max(n, 256), dtype=torch.uint8, device="cuda")
-    out = dw.new_out()
+    out = dw.new_out() if out is None else out
     lra.lora_attn_varlen(dw.q, dw.k_base, dw.v_base, dw.block_tables, dw.context_lens, dw.max_context_len,
                          dw.cu_q_lens, dw.max_q_len, S_dec, dw.group_offsets, dw.agent_ids, dw.lk_ptrs, dw.lv_ptrs,
                          dw.bk_ptrs, dw.bv_ptrs, dw.ranks, dw.max_rank, w.n_agents, w.Hkv, w.sm_scale, w.theta, out, ws,

@@ -103,6 +103,27 @@ def _start_shifts_rotation(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
     return K, V
 
 
+def _base_updated_in_place(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    """Adds the adapter terms into the caller's base arrays (an aliasing
+    mistake: the next agent over the same base sees this agent's terms)."""
+    K, V = _orig_mat(kb, vb, lk, lv, bk, bv, theta, adapter_start)
+    if isinstance(kb, np.ndarray) and kb.dtype == np.float64:
+        kb += K - kb
+        vb += V - vb
+        return kb, vb
+    return K, V
+
+
+def _value_adapter_rank_reversed(kb, vb, lk, lv, bk, bv, theta, adapter_start=0):
+    """Pairs rank k of L_v with row r-1-k of B_v (a transposed operand)."""
+    return _orig_mat(kb, vb, lk, lv, bk, None if bv is None else np.asarray(bv)[::-1], theta, adapter_start)
+
+
+def _adapter_head_swapped(l_rows, b, Hkv, d):
+    """Feeds KV head h from the columns of head Hkv-1-h."""
+    return _orig_adapter(l_rows, b, Hkv, d)[:, ::-1, :]
+
+
 def _gqa_modulo(j, Hq, Hkv):
     return j % Hkv
 
@@ -140,6 +161,9 @@ MUTATIONS = {
     "adapter_start_on_keys_only": ("materialise_kv", _start_keys_only),
     "adapter_start_rotation_relative": ("materialise_kv", _start_shifts_rotation),
     "gqa_modulo_mapping": ("kv_head_of", _gqa_modulo),
+    "base_updated_in_place": ("materialise_kv", _base_updated_in_place),
+    "value_adapter_rank_reversed": ("materialise_kv", _value_adapter_rank_reversed),
+    "adapter_heads_swapped": ("adapter_term", _adapter_head_swapped),
     "causal_off_by_one": ("attend", _causal_exclusive),
     "missing_softmax_scale": ("attend", _no_scale),
     "build_columns_reversed": ("lr_cache_build", _build_transposed),
@@ -147,8 +171,7 @@ MUTATIONS = {
 }
 
 
-@pytest.mark.parametrize("name", sorted(MUTATIONS))
-def test_mutation_is_caught(name, monkeypatch):
+def _failing_pins(name, monkeypatch):
     attr, fn = MUTATIONS[name]
     monkeypatch.setattr(O, attr, fn)
     failed = []
@@ -157,4 +180,24 @@ def test_mutation_is_caught(name, monkeypatch):
             pin(O)
         except AssertionError:
             failed.append(pin.__name__)
-    assert failed, f"no pin catches mutation {name}"
+    return failed
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, monkeypatch):
+    assert _failing_pins(name, monkeypatch), f"no pin catches mutation {name}"
+
+
+# pins that must each catch a particular planted mistake on their own
+OWN_CATCH = [
+    ("pin_reorder_equals_materialised", "value_adapter_rank_reversed"),
+    ("pin_reorder_equals_materialised", "rotate_value_adapter"),
+    ("pin_shared_base_unchanged", "base_updated_in_place"),
+    ("pin_bruteforce_tiny", "adapter_heads_swapped"),
+    ("pin_bruteforce_tiny", "adapter_head_major_columns"),
+]
+
+
+@pytest.mark.parametrize("pin,name", OWN_CATCH, ids=[f"{p}-{m}" for p, m in OWN_CATCH])
+def test_pin_catches_its_mutation(pin, name, monkeypatch):
+    assert pin in _failing_pins(name, monkeypatch)
