@@ -45,7 +45,9 @@ def test_build_matches_oracle(shape):
     rne = torch.from_numpy(ref).float().to(torch.bfloat16).float().numpy()
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
     off_mid = np.abs(np.abs(ref - rne) - ulp / 2) > 1e-3 * ulp
-    assert (L == rne)[off_mid].mean() >= 0.95
+    rate = float((L == rne)[off_mid].mean())
+    print(f"[rne] {shape}: {rate:.4f} of off-midpoint elements equal RNE(fp64)", flush=True)
+    assert rate >= 0.99
 
 
 def test_build_paged_stores_bit_exact():
