@@ -369,7 +369,7 @@ def leg_prefill(K, W):
         seg = w.segments[1 + a]
         ids = torch.from_numpy(seg.blocks.astype("int64"))
         slots.append((ids[:, None] * 16 + torch.arange(16)[None, :]).reshape(-1)[: seg.T].cuda())
-    bws = torch.empty(lra.lr_cache_build_workspace_size(512, 4096, 16), dtype=torch.uint8, device="cuda")
+    bws = torch.zeros(lra.lr_cache_build_workspace_size(512, 4096, 16), dtype=torch.uint8, device="cuda")
     out = dw.new_out()
 
     def build_all():
@@ -500,8 +500,8 @@ def leg_lr_multi(K, W, n_agents=4, rank=16):
     lays = [lra.LRA_L_TOKEN_MAJOR, lra.LRA_L_RANK_MAJOR] * n_agents
     pools = [torch.zeros((nb, 16, rank) if l == 0 else (nb, rank, 16), dtype=torch.bfloat16, device="cuda")
              for l in lays]
-    ws = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, ncols), dtype=torch.uint8, device="cuda")
-    ws1 = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, rank), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, ncols), dtype=torch.uint8, device="cuda")
+    ws1 = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, rank), dtype=torch.uint8, device="cuda")
 
     def multi():
         lra.lr_cache_build_multi(Xd, Ad, cols, pools, lays, slots, ws)

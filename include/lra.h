@@ -42,7 +42,8 @@
  *   context length and block-table row. It synchronises `stream` to read
  *   the result and returns LRA_ERR_INVALID_ARG naming the first failing
  *   check before the attention kernels run (so it cannot be captured in a
- *   graph).
+ *   graph). For lr_cache_build and lr_cache_build_multi it checks, before the
+ *   launch, that the workspace's tile counters are zero.
  * - dtype applies to every floating-point tensor of a call (q, pools,
  *   adapters, out; X, A, L for the cache build). Accumulation is fp32.
  *
@@ -68,7 +69,7 @@
 extern "C" {
 #endif
 
-#define LRA_VERSION 300
+#define LRA_VERSION 400
 
 typedef enum lra_status {
   LRA_OK = 0,
@@ -108,8 +109,16 @@ const char* lra_last_error(void);
  *   slot skips the row. Columns [0, n_cols) of each row are written.
  *   dtype: LRA_BF16. hidden % 8 == 0, 1 <= n_cols <= 512, ldx, lda >= their
  *   widths, X 16-byte aligned with ldx % 8 == 0.
- *   workspace: lr_cache_build_workspace_size(...) bytes, which is 0 (the sums
- *   over hidden stay inside each workgroup); workspace may be NULL.
+ *   workspace: lr_cache_build_workspace_size(...) bytes of device memory,
+ *   16-byte aligned (0 bytes, and NULL allowed, when hidden <= 512). The
+ *   hidden dimension is summed in slices of 512 by separate workgroups; the
+ *   workspace holds their fp32 partial sums and, in its first 4096 bytes, one
+ *   counter per output tile. Those 4096 bytes must be zero the first time a
+ *   workspace is used (allocate it zero-filled); every call leaves them zero
+ *   again, so the same workspace serves any later build of any size up to
+ *   the one it was sized for. Calls that overlap in time must use different
+ *   workspaces. The partial sums of a column are added in slice order, so a
+ *   result does not depend on the order in which workgroups finish.
  * ---------------------------------------------------------------------- */
 size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_cols);
 
@@ -135,7 +144,8 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
  *   device pointers; group_layouts (host) int32 [n_groups] of lra_l_layout.
  *   1 <= n_groups <= 64. slot_mapping: int64 [n_tokens], required.
  *   Sizes, dtype and workspace as for lr_cache_build (the workspace query is
- *   lr_cache_build_workspace_size with the total n_cols).
+ *   lr_cache_build_workspace_size with the total n_cols; its first 4096 bytes
+ *   zero-filled before first use).
  * ---------------------------------------------------------------------- */
 int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda, int32_t n_groups,
                          const int32_t* group_cols, void* const* group_pools, const int32_t* group_layouts,

@@ -156,7 +156,9 @@ def lr_cache_build(X, A, L, workspace, *, slot_mapping=None, l_layout=LRA_L_TOKE
                    stream=None):
     """L = X A. X [n, hidden] and A [hidden, n_cols] bf16 tensors (row strides
     taken from the tensors); L a bf16 tensor: dense [n, >=n_cols] or a paged
-    pool addressed through ``slot_mapping`` (int64 [n])."""
+    pool addressed through ``slot_mapping`` (int64 [n]). ``workspace``: at
+    least lr_cache_build_workspace_size(n, hidden, n_cols) bytes, zero-filled
+    before its first use (each call leaves its counters zero again)."""
     n, hidden = X.shape
     n_cols = A.shape[1] if n_cols is None else n_cols
     if ldl is None:

@@ -37,6 +37,9 @@
 // per-column part (a table of 16 x 64 pairs built once per workgroup), so
 // no transcendental is evaluated per element.
 #pragma once
+#ifndef LRA_RT_INNER
+#define LRA_RT_INNER 1
+#endif
 #include <type_traits>
 
 #include "device_common.h"
@@ -114,12 +117,30 @@ __device__ __forceinline__ bool decode_item_rows(const DecodeArgs& a, int logica
   int rem = logical;
   w.h = rem % a.Hkv;
   rem /= a.Hkv;
+#if LRA_RT_INNER
+  w.rt = rem % a.row_tiles;
+  rem /= a.row_tiles;
+  w.c = rem % a.nsplit;
+  w.g = rem / a.nsplit;
+#else
   w.c = rem % a.nsplit;
   rem /= a.nsplit;
   w.rt = rem % a.row_tiles;
   w.g = rem / a.row_tiles;
-  w.s_first = a.group_offsets ? sload(a.group_offsets + w.g) : w.g;
-  const int s_end = a.group_offsets ? sload(a.group_offsets + w.g + 1) : w.g + 1;
+#endif
+  // group_offsets rise from 0 to S, so the first group starts at 0 and the
+  // last ends at S without a load (one dependent round trip fewer for a call
+  // with one group)
+  int s_end;
+  if (a.group_offsets) {
+    w.s_first = 0;
+    s_end = a.S;
+    if (w.g > 0) w.s_first = sload(a.group_offsets + w.g);
+    if (w.g + 1 < a.num_groups) s_end = sload(a.group_offsets + w.g + 1);
+  } else {
+    w.s_first = w.g;
+    s_end = w.g + 1;
+  }
   w.s0 = w.s_first + w.rt * a.apt;
   w.ns = min(a.apt, s_end - w.s0);
   w.tile_id = (w.g * a.row_tiles + w.rt) * a.Hkv + w.h;

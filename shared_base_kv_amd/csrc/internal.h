@@ -69,6 +69,8 @@ struct DecodeArgs {
 
 constexpr int kMaxBuildGroups = 64;  // destination column groups of one cache build
 constexpr int kMaxBuildCols = 512;   // columns of A in one cache build
+constexpr int kBuildSlice = 512;     // hidden values summed by one cache-build workgroup
+constexpr int kBuildCounterSlots = 1024;  // tile counters at the start of the cache-build workspace
 
 // One cache build: L = X A, columns [group_col[g], group_col[g+1]) of the
 // product going to destination g (a dense matrix or a paged pool).
@@ -84,7 +86,14 @@ struct BuildArgs {
   int32_t group_layout[kMaxBuildGroups];  // 0 token-major (row stride group_ld), 1 rank-major
   int64_t group_ld[kMaxBuildGroups];
   void* group_dst[kMaxBuildGroups];
+  int32_t ksplit;     // slices of the hidden dimension (ceil(hidden / kBuildSlice))
+  int* counters;      // [kBuildCounterSlots] tile counters, zero between launches (ksplit > 1)
+  float* partials;    // [tiles of a launch][ksplit][256] fp32 partial sums (ksplit > 1)
 };
+
+// Cache-build workspace: counters, then the partial sums of one launch.
+size_t build_workspace_bytes(int n_tokens, int hidden, int n_cols);
+int build_tiles_per_launch(int col_tiles);
 
 struct PrefillArgs {
   const void* q;

@@ -226,6 +226,32 @@ int debug_check(const CheckArgs& c, const char* name, hipStream_t stream) {
   return LRA_OK;
 }
 
+// the cache-build workspace's tile counters must all be zero on entry
+__global__ void check_build_counters_kernel(const int* counters, int n) {
+  const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+  if (i < n && counters[i] != 0) atomicMin(&g_check, i);
+}
+
+int debug_check_build(const int* counters, const char* name, hipStream_t stream) {
+  if (!counters) return LRA_OK;
+  const int none = kNoFailure;
+  int got = kNoFailure;
+  hipError_t e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_check), &none, sizeof(none), 0, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(check_build_counters_kernel, dim3((kBuildCounterSlots + 255) / 256), dim3(256), 0, stream,
+                       counters, kBuildCounterSlots);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess)
+    e = hipMemcpyFromSymbolAsync(&got, HIP_SYMBOL(g_check), sizeof(got), 0, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "%s: input check failed to run: %s", name, hipGetErrorString(e));
+  if (got != kNoFailure)
+    return fail(LRA_ERR_WORKSPACE, "%s: workspace tile counter %d is not zero (zero-fill the workspace before first use)",
+                name, got);
+  return LRA_OK;
+}
+
 CheckArgs decode_check_args(const DecodeArgs& a, int max_context_len, int max_rank, int N_agents, int dtype,
                             const int32_t* varlen_cu_q_lens = nullptr) {
   const bool adapted = a.bk || a.bv;
@@ -261,11 +287,8 @@ const char* lra_last_error(void) { return g_err; }
 
 // --------------------------------------------------------------------------
 size_t lr_cache_build_workspace_size(int32_t n_tokens, int32_t hidden, int32_t n_cols) {
-  // one launch sums over the hidden dimension inside each workgroup: no workspace
-  (void)n_tokens;
-  (void)hidden;
-  (void)n_cols;
-  return 0;
+  if (n_tokens < 0 || hidden < 1 || n_cols < 1 || n_cols > kMaxBuildCols) return 0;
+  return build_workspace_bytes(n_tokens, hidden, n_cols);
 }
 
 }  // extern "C"
@@ -285,10 +308,19 @@ int launch_build(BuildArgs& a, const char* name, int32_t dtype, void* workspace,
                 (long long)a.lda);
   if ((long long)a.hidden * a.lda * 2 > 0x7fffffffLL || (long long)16 * a.ldx * 2 > 0x7fffffffLL)
     return fail(LRA_ERR_UNSUPPORTED, "%s: A spans more than 2 GiB (hidden * lda), or 16 rows of X do (ldx)", name);
-  (void)workspace;  // the workspace size is 0: any pointer (or NULL) is accepted
-  (void)workspace_bytes;
   a.row_tiles = ceil_div(a.n_tokens, 16);
   a.col_tiles = ceil_div(a.n_cols, 16);
+  a.ksplit = ceil_div(a.hidden, kBuildSlice);
+  const size_t need = build_workspace_bytes(a.n_tokens, a.hidden, a.n_cols);
+  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    return fail(LRA_ERR_WORKSPACE, "%s: workspace of %zu bytes (16-byte aligned, counters zero-filled) needed (got %zu)",
+                name, need, workspace_bytes);
+  a.counters = need ? (int*)workspace : nullptr;
+  a.partials = need ? (float*)((char*)workspace + (size_t)kBuildCounterSlots * sizeof(int)) : nullptr;
+#ifdef LRA_DEBUG_CHECKS
+  const int rc = debug_check_build(a.counters, name, (hipStream_t)stream);
+  if (rc != LRA_OK) return rc;
+#endif
   const hipError_t e = launch_lr_build_bf16(a, (hipStream_t)stream);
   if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
   return ok();

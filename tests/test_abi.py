@@ -111,7 +111,21 @@ def test_build_rejects_bad_arguments():
     assert call(lay=1) == B.LRA_ERR_INVALID_ARG  # rank-major needs a slot mapping
     assert call(ldl=8) == B.LRA_ERR_INVALID_ARG
     assert call(n=0) == B.LRA_OK
-    assert lra.lr_cache_build_workspace_size(512, 4096, 16) == 0  # one launch, no partial sums
+    assert call(ws=None) == B.LRA_ERR_WORKSPACE  # hidden 4096 is summed in 8 slices
+    assert call(wsb=4096) == B.LRA_ERR_WORKSPACE
+
+
+def test_build_workspace_size():
+    """Counters (4096 bytes) plus one fp32 16x16 partial per tile and slice of
+    512 hidden values; nothing when the hidden size fits one slice."""
+    f = lra.lr_cache_build_workspace_size
+    assert f(512, 4096, 16) == 4096 + 32 * 1 * 8 * 1024
+    assert f(512, 4096, 128) == 4096 + 32 * 8 * 8 * 1024
+    assert f(37, 520, 8) == 4096 + 3 * 1 * 2 * 1024
+    assert f(5000, 512, 16) == 0 and f(1, 8, 1) == 0
+    # at most 1024 tiles' partials (larger builds run in several launches)
+    assert f(1 << 16, 4096, 512) == 4096 + 1024 * 8 * 1024
+    assert f(-1, 4096, 16) == 0 and f(4, 4096, 600) == 0
 
 
 def test_prefill_rejects_bad_arguments():

@@ -17,10 +17,12 @@ def _dev_bf16(x):
     return torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _build(X, A, **kw):
+def _build(X, A, ws=None, **kw):
     n, hidden = X.shape
     ncols = A.shape[1]
-    ws = torch.empty(max(lra.lr_cache_build_workspace_size(n, hidden, ncols), 16), dtype=torch.uint8, device="cuda")
+    if ws is None:
+        ws = torch.zeros(max(lra.lr_cache_build_workspace_size(n, hidden, ncols), 16), dtype=torch.uint8,
+                         device="cuda")
     L = kw.pop("L", None)
     if L is None:
         L = torch.full((n, ncols), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -104,11 +106,11 @@ def test_multi_build_equals_single_builds_bit_exact(shape):
                 for w, lay in zip(widths, lays)]
 
     multi = pools()
-    ws = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, cols[-1]), dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, cols[-1]), dtype=torch.uint8, device="cuda")
     lra.lr_cache_build_multi(Xd, Ad, cols, multi, lays, sm, ws)
     single = pools()
     for g, (w, lay) in enumerate(zip(widths, lays)):
-        wsg = torch.empty(lra.lr_cache_build_workspace_size(n, hidden, w), dtype=torch.uint8, device="cuda")
+        wsg = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, w), dtype=torch.uint8, device="cuda")
         lra.lr_cache_build(Xd, Ad[:, cols[g]:cols[g + 1]], single[g], wsg, slot_mapping=sm, l_layout=lay, ldl=w,
                            n_cols=w)
     torch.cuda.synchronize()
@@ -123,3 +125,22 @@ def test_multi_build_equals_single_builds_bit_exact(shape):
         assert row_rel_err(got[slots[keep]], refs[g][keep]) <= TOL_BF16, g
         untouched = sorted(set(range(nb * 16)) - set(int(s) for s in slots[keep]))
         assert not rows[untouched].any(), g
+
+
+def test_build_reuses_workspace_across_calls():
+    """Twelve builds in a row, of changing data and sizes, on one workspace
+    (zero-filled once): every result matches the oracle and is bit-identical
+    to the same build on a freshly zero-filled workspace, and the tile
+    counters are back at zero after each call (no slice reads another call's
+    partial sums or counts)."""
+    big = lra.lr_cache_build_workspace_size(512, 4096, 64)
+    ws = torch.zeros(big, dtype=torch.uint8, device="cuda")
+    shapes = [(512, 4096, 16), (300, 2048, 64), (17, 4096, 8), (512, 4096, 64), (64, 1032, 40), (1, 4096, 16)] * 2
+    for i, (n, hidden, ncols) in enumerate(shapes):
+        X, A = build_inputs(n, hidden, ncols, seed=1000 + i)
+        print(f"[case] build {i}: n={n} hidden={hidden} cols={ncols}", flush=True)
+        L = _build(X, A, ws=ws)
+        fresh = _build(X, A)
+        assert torch.equal(L.view(torch.int16), fresh.view(torch.int16)), i
+        assert row_rel_err(L.float().cpu().numpy(), oracle.lr_cache_build(X, A)) <= TOL_BF16, i
+        assert not ws[:4096].any(), i

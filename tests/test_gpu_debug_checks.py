@@ -131,3 +131,25 @@ def test_bad_varlen_input_is_reported(use_debug):
         run_varlen(mw, 4)
     assert e.value.code == B.LRA_ERR_INVALID_ARG
     assert "prefill part" in str(e.value) and "agent id" in str(e.value)
+
+
+def test_build_workspace_counters_checked(use_debug):
+    """The cache build's tile counters must be zero on entry (the workspace is
+    zero-filled before first use); the debug library reports a nonzero one
+    before the build runs, leaving L untouched."""
+    import numpy as np
+
+    from workloads import bf16_bits, build_inputs
+
+    print("[case] debug library, cache build with a nonzero tile counter", flush=True)
+    X, A = build_inputs(64, 1024, 16, seed=3)
+    dev = lambda x: torch.from_numpy(bf16_bits(x).view(np.int16)).view(torch.bfloat16).cuda()  # noqa: E731
+    ws = torch.zeros(lra.lr_cache_build_workspace_size(64, 1024, 16), dtype=torch.uint8, device="cuda")
+    ws[8:12] = 1  # counter 2
+    L = torch.full((64, 16), SENTINEL, dtype=torch.bfloat16, device="cuda")
+    use_debug()
+    with pytest.raises(lra.LraError) as e:
+        lra.lr_cache_build(dev(X), dev(A), L, ws)
+        torch.cuda.synchronize()
+    assert e.value.code == B.LRA_ERR_WORKSPACE and "counter 2" in str(e.value), str(e.value)
+    assert bool((L == SENTINEL).all())

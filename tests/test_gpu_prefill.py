@@ -110,7 +110,7 @@ def test_build_then_prefill_pipeline():
         seg = w.segments[1 + a]
         slots = (seg.blocks.astype(np.int64)[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)[: seg.T]
         sm = torch.from_numpy(slots).cuda()
-        ws = torch.empty(lra.lr_cache_build_workspace_size(seg.T, hidden, 16), dtype=torch.uint8, device="cuda")
+        ws = torch.zeros(lra.lr_cache_build_workspace_size(seg.T, hidden, 16), dtype=torch.uint8, device="cuda")
         lra.lr_cache_build(dev(Xs[a]), dev(Ak), dw.lk_pools[0], ws, slot_mapping=sm, l_layout=lra.LRA_L_TOKEN_MAJOR,
                            ldl=16)
         lra.lr_cache_build(dev(Xs[a]), dev(Av), dw.lv_pools[0], ws, slot_mapping=sm, l_layout=lra.LRA_L_RANK_MAJOR)
