@@ -37,9 +37,6 @@
 // per-column part (a table of 16 x 64 pairs built once per workgroup), so
 // no transcendental is evaluated per element.
 #pragma once
-#ifndef LRA_RT_INNER
-#define LRA_RT_INNER 1
-#endif
 #include <type_traits>
 
 #include "device_common.h"
@@ -109,25 +106,20 @@ struct WorkItem {
 };
 
 // Logical work item -> (group, row tile, split, KV head). The KV head varies
-// fastest, so the heads of one split are consecutive items and share an XCD
-// (the low-rank rows of those tokens, shared by every head, reach that L2 once).
+// fastest, then the row tile, so the heads and row tiles of one split are
+// consecutive items on one XCD (the low-rank rows of those tokens, shared by
+// every head, and the base blocks, shared by the row tiles of a group, reach
+// that L2 once).
 // First part: the group's sequences and the row tile's slots (false: the
 // tile has no sequences).
 __device__ __forceinline__ bool decode_item_rows(const DecodeArgs& a, int logical, WorkItem& w) {
   int rem = logical;
   w.h = rem % a.Hkv;
   rem /= a.Hkv;
-#if LRA_RT_INNER
   w.rt = rem % a.row_tiles;
   rem /= a.row_tiles;
   w.c = rem % a.nsplit;
   w.g = rem / a.nsplit;
-#else
-  w.c = rem % a.nsplit;
-  rem /= a.nsplit;
-  w.rt = rem % a.row_tiles;
-  w.g = rem / a.row_tiles;
-#endif
   // group_offsets rise from 0 to S, so the first group starts at 0 and the
   // last ends at S without a load (one dependent round trip fewer for a call
   // with one group)
