@@ -165,8 +165,11 @@ int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda,
  *                 the block-table row and context length of the first one;
  *                 the base cache is then read once for all of them (the
  *                 shared base component of LRAgent's abstract). At most
- *                 16 / (Hq/Hkv) sequences of a group share one pass; larger
- *                 groups are served in several passes.
+ *                 min(8, 16 / (Hq/Hkv), 256 / r_pad) sequences of a group
+ *                 share one pass (r_pad: max_rank rounded up to 16, 32 or 64);
+ *                 larger groups are served in several passes, whose reads of
+ *                 the base are placed on one XCD so that the later ones can
+ *                 hit its L2.
  *   agent_ids     int32 [S], in [0, N_agents), or -1 for a sequence without
  *                 an adapter (it attends over the base cache alone; PReCache
  *                 Figure 1 caption batches such adapter-free paths with
@@ -255,14 +258,14 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
                       int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Decode rows and prefill chunks in one launch (a serving step that mixes
+ * Decode rows and prefill chunks in one call (a serving step that mixes
  * decoding sequences with prefill chunks: PReCache, Figure 1 caption, an
  * agent's new segment prefilled while other agents decode; LRAgent: Efficient
  * KV Cache Sharing for Multi-LoRA LLM Agents, abstract, concurrent agents on
  * one shared base). Sequences 0 .. S_dec - 1 decode (one query each), the
- * rest are prefill chunks. One grid runs both kinds of workgroups; each row's
- * result is bit-identical to what lora_attn_decode (for the first S_dec
- * sequences) and lora_attn_prefill (for the rest) would write.
+ * rest are prefill chunks. Each row's result is bit-identical to what
+ * lora_attn_decode (for the first S_dec sequences) and lora_attn_prefill (for
+ * the rest) would write.
  *
  *   q, out        [cu_q_lens[S], Hq, d]: decode sequence s < S_dec owns row s,
  *                 prefill sequence s its rows cu_q_lens[s] .. cu_q_lens[s+1]-1.
@@ -278,8 +281,8 @@ int lora_attn_prefill(const void* q, const void* k_base, const void* v_base, con
  *   Everything else as for decode and prefill. dtype: LRA_BF16, d = 128.
  *   workspace     lora_attn_varlen_workspace_size(...) bytes (the decode
  *                 part's split records), as for decode.
- *   A call is one main kernel (decode and prefill workgroups), plus the
- *   decode combine kernel when a decode context is split.
+ *   A call runs the prefill kernel for the chunks, then the decode kernel
+ *   (and its combine kernel when a decode context is split) on `stream`.
  * ---------------------------------------------------------------------- */
 size_t lora_attn_varlen_workspace_size(int32_t S, int32_t S_dec, int32_t num_groups, int32_t Hq, int32_t Hkv, int32_t d,
                                        int32_t max_rank, int32_t max_context_len, int32_t dtype);

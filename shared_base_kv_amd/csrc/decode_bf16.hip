@@ -121,7 +121,6 @@ bool launch_variant(const DecodeArgs& a, int rp, int na, dim3 grid, hipStream_t 
     case 1602: launch_main<16, 2, KAD, VAD>(a, grid, stream); return true;
     case 1604: launch_main<16, 4, KAD, VAD>(a, grid, stream); return true;
     case 1608: launch_main<16, 8, KAD, VAD>(a, grid, stream); return true;
-    case 1616: launch_main<16, 16, KAD, VAD>(a, grid, stream); return true;
     case 3201: launch_main<32, 1, KAD, VAD>(a, grid, stream); return true;
     case 3202: launch_main<32, 2, KAD, VAD>(a, grid, stream); return true;
     case 3204: launch_main<32, 4, KAD, VAD>(a, grid, stream); return true;
@@ -166,29 +165,16 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t s
   return hipGetLastError();
 }
 
+// A serving step with decoding sequences and prefill chunks: the prefill
+// kernel, then the decode kernels, on one stream. Each row is computed by the
+// same kernel as in the separate calls, so it is bit-identical to them.
 hipError_t launch_varlen_bf16(const DecodeArgs& d, int rp, int na, const PrefillArgs& p, hipStream_t stream) {
-  // each part's workgroups are dealt over the XCDs as in its own call, so both
-  // parts start at a multiple of the XCD count
-  const int n_dec = d.S > 0 ? (d.n_work + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
-  const int n_pre = p.S > 0 ? (p.Hkv * p.S * p.q_tiles + kNumXcd - 1) / kNumXcd * kNumXcd : 0;
-  if (n_dec + n_pre == 0) return hipSuccess;
-  const dim3 grid(n_dec + n_pre);
-  const bool kad = d.bk != nullptr, vad = d.bv != nullptr;
-  bool launched;
-  if (kad && vad)
-    launched = launch_mixed_bf16_kv(d, p, rp, na, n_pre, grid, stream);
-  else if (vad)
-    launched = launch_mixed_bf16_v(d, p, rp, na, n_pre, grid, stream);
-  else if (kad)
-    launched = launch_mixed_bf16_k(d, p, rp, na, n_pre, grid, stream);
-  else
-    launched = launch_mixed_bf16_none(d, p, n_pre, grid, stream);
-  if (!launched) return hipErrorInvalidValue;
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || d.S == 0 || d.nsplit <= 1) return e;
-  const int n_rows = d.num_groups * d.row_tiles * d.Hkv * 16;
-  hipLaunchKernelGGL(decode_bf16_combine, dim3(n_rows), dim3(64), 0, stream, d);
-  return hipGetLastError();
+  if (p.S > 0) {
+    const hipError_t e = launch_prefill_bf16(p, stream);
+    if (e != hipSuccess) return e;
+  }
+  if (d.S > 0) return launch_decode_bf16(d, rp, na, stream);
+  return hipSuccess;
 }
 #endif
 

@@ -1,6 +1,5 @@
 // Types and helpers of the decode workgroup; its statements are in
-// decode_bf16_body.inc, included by the kernels that run it (decode_bf16.hip:
-// the decode call; mixed_bf16.hip: decode and prefill in one grid).
+// decode_bf16_body.inc, included by the decode kernel (decode_bf16.hip).
 //
 // What is computed (LRAgent: Efficient KV Cache Sharing for Multi-LoRA LLM
 // Agents, abstract): keys and values are a shared base part plus an adapter

@@ -14,9 +14,14 @@ constexpr int kNumXcd = 8;       // workgroups are dealt round-robin over XCDs
 constexpr int kDecodeWaves = 8;  // waves per decode workgroup
 constexpr int kWaveBlocks = 2;   // cache blocks per wave in the smallest split
 constexpr int kMaxSplits = 64;   // split-K partitions per (group, head, row tile)
+constexpr int kMaxTileAgents = 8;  // sequences of one decode row tile
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxSplitBlocks = 256;  // cache blocks in one split (split <= 4096 tokens)
-constexpr int kPrefillRows = 256;     // query rows (tokens x query heads of one KV head) per prefill workgroup
+// 16-row tiles per prefill wave (8 waves per workgroup): two, or one at rank
+// 64 with both adapters
+constexpr int prefill_row_tiles(int rp, bool kad, bool vad) { return (rp == 64 && kad && vad) ? 1 : 2; }
+// query rows (tokens x query heads of one KV head) per prefill workgroup
+constexpr int prefill_rows(int rp, bool kad, bool vad) { return 8 * 16 * prefill_row_tiles(rp, kad, vad); }
 
 // Decode launch plan: derived on the host from sizes only, so the workspace
 // query and the launch agree.
@@ -130,15 +135,7 @@ bool launch_decode_bf16_kv(const DecodeArgs& a, int rp, int na, dim3 grid, hipSt
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_lr_build_bf16(const BuildArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
-// prefill chunks (n_pre workgroups first) and decode rows in one grid, then
-// the decode combine when the decode part has split records
+// prefill chunks, then decode rows, on one stream
 hipError_t launch_varlen_bf16(const DecodeArgs& d, int rp, int na, const PrefillArgs& p, hipStream_t stream);
-bool launch_mixed_bf16_kv(const DecodeArgs& d, const PrefillArgs& p, int rp, int na, int n_pre, dim3 grid,
-                          hipStream_t stream);
-bool launch_mixed_bf16_v(const DecodeArgs& d, const PrefillArgs& p, int rp, int na, int n_pre, dim3 grid,
-                         hipStream_t stream);
-bool launch_mixed_bf16_k(const DecodeArgs& d, const PrefillArgs& p, int rp, int na, int n_pre, dim3 grid,
-                         hipStream_t stream);
-bool launch_mixed_bf16_none(const DecodeArgs& d, const PrefillArgs& p, int n_pre, dim3 grid, hipStream_t stream);
 
 }  // namespace lra

@@ -53,6 +53,7 @@ DecodePlan decode_plan(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
   }
   p.apt = 16 / p.G;
   if (p.apt > 256 / p.rp) p.apt = 256 / p.rp;  // staged B_k^T of a tile fits 64 KB of LDS
+  if (p.apt > kMaxTileAgents) p.apt = kMaxTileAgents;  // wider tiles would not fit the registers
   const int max_group = S - num_groups + 1;
   p.row_tiles = ceil_div(max_group, p.apt);
   p.na = 1;
@@ -439,8 +440,8 @@ int make_prefill_args(PrefillArgs& a, const void* q, const void* k_base, const v
   a.d = d;
   a.G = Hq / Hkv;
   a.max_q_len = max_q_len;
-  a.q_tiles = ceil_div(max_q_len, kPrefillRows / (Hq / Hkv));
   a.rp = pad_rank(max_rank);
+  a.q_tiles = ceil_div(max_q_len, prefill_rows(a.rp, b_k != nullptr, b_v != nullptr) / (Hq / Hkv));
   a.sm_scale = sm_scale;
   a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.rope = rope_theta > 0.f;

@@ -1,6 +1,5 @@
 // Body of the prefill workgroup (one query tile of one sequence and KV
-// head); the kernels that run it are in prefill_bf16.hip (the prefill call)
-// and mixed_bf16.hip (decode and prefill in one grid).
+// head); the kernel that runs it is in prefill_bf16.hip.
 //
 // Each sequence appends a chunk of q_len new tokens after its context
 // (PReCache, Figure 1 caption: an agent's turn is prefilled over its new
@@ -15,8 +14,10 @@
 //     space, and C B_v is applied once per row after the key loop.
 //
 // Work decomposition: one workgroup = (sequence s, KV head h, query tile);
-// a query tile has 256 rows = 256/G query tokens x G query heads. Each of the
-// 8 waves (two per SIMD) consumes 32 query rows (scores, softmax, P V on the
+// a query tile has 256 rows = 256/G query tokens x G query heads (128 rows at
+// rank 64 with both adapters, whose rank-space accumulators would not fit the
+// registers beside two row tiles). Each of the 8 waves (two per SIMD)
+// consumes 32 (16) query rows (scores, softmax, P V on the
 // matrix cores) and also produces part of the next tile: with a key adapter
 // every wave loads and rebuilds half of one 16-key cache block (half of the
 // rotary pairs and of the V^T rows), so the rebuild's registers fit beside
@@ -52,7 +53,6 @@ namespace pf {
 namespace {
 
 constexpr int D = 128;
-constexpr int kRows = kPrefillRows;  // query rows per workgroup
 constexpr int kTile = 64;      // keys per tile (4 cache blocks)
 constexpr int kKPitch = D + 16;         // LDS row pitch of the key tile (bf16; 72 dwords: 16-byte reads conflict-free)
 constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
