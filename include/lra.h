@@ -230,6 +230,30 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
                      int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Decode attention without a workspace, for callers that cannot allocate
+ * device memory around the call (code being captured into a HIP graph,
+ * tight serving loops, harnesses that forbid allocation). Arguments, result
+ * and kernels are those of lora_attn_decode, less the workspace: the split
+ * records go to a fixed device array of 16 MiB that the library holds on
+ * each GPU it runs on until the process ends (its address is looked up once
+ * per device, on the first call for that device). No call allocates or
+ * frees anything.
+ *   A call whose records need more than 16 MiB
+ *   (lora_attn_decode_workspace_size) returns LRA_ERR_UNSUPPORTED before any
+ *   HIP call. Every record a call reads is written by the same call, so the
+ *   array needs no clearing; it keeps the last call's contents. All calls on
+ *   one GPU share the array: calls that overlap in time on one GPU race and
+ *   give undefined results (serialise them, e.g. on one stream).
+ * ---------------------------------------------------------------------- */
+int lora_attn_decode_noalloc(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                             const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
+                             const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools,
+                             const void* const* b_k, const void* const* b_v, const int32_t* ranks, int32_t max_rank,
+                             int32_t S, int32_t N_agents, int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                             float sm_scale, float rope_theta, int32_t dtype, void* out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Prefill attention: a chunk of q_len_s = cu_q_lens[s+1] - cu_q_lens[s]
  * new tokens per sequence, already written to the caches, attends causally:
  * query i of sequence s sits at position T_s - q_len_s + i and sees keys

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     LraError,
     load,
     lora_attn_decode,
+    lora_attn_decode_noalloc,
     lora_attn_decode_workspace_size,
     lora_attn_prefill,
     lora_attn_prefill_workspace_size,

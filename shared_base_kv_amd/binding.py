@@ -34,6 +34,7 @@ EXPORTS = (
     "lr_cache_build_multi",
     "lora_attn_decode_workspace_size",
     "lora_attn_decode",
+    "lora_attn_decode_noalloc",
     "lora_attn_prefill_workspace_size",
     "lora_attn_prefill",
     "lora_attn_varlen_workspace_size",
@@ -97,6 +98,8 @@ def _open(path: str) -> ctypes.CDLL:
             _i32, _i32, _i32, _i32, _f32, _f32, _i32, _p, _p, _sz, _p]
     lib.lora_attn_decode.restype = ctypes.c_int
     lib.lora_attn_decode.argtypes = attn
+    lib.lora_attn_decode_noalloc.restype = ctypes.c_int
+    lib.lora_attn_decode_noalloc.argtypes = attn[:-3] + [_p]  # no workspace, workspace_bytes
     lib.lora_attn_prefill_workspace_size.restype = _sz
     lib.lora_attn_prefill_workspace_size.argtypes = size8
     lib.lora_attn_prefill.restype = ctypes.c_int
@@ -205,6 +208,20 @@ def lora_attn_decode(q, k_base, v_base, block_tables, context_lens, max_context_
         _ptr(l_v_pools),
         _ptr(b_k), _ptr(b_v), _ptr(ranks), max_rank, S, n_agents, Hq, Hkv, d, 16, sm_scale, rope_theta,
         _dtype_code(q), _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def lora_attn_decode_noalloc(q, k_base, v_base, block_tables, context_lens, max_context_len, group_offsets, agent_ids,
+                             l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank, n_agents, Hkv, sm_scale, rope_theta, out,
+                             stream=None, adapter_start=None):
+    """lora_attn_decode without a workspace: the split records go to the
+    library's fixed 16 MiB device array (calls overlapping on one GPU race)."""
+    S, Hq, d = q.shape
+    num_groups = (group_offsets.numel() - 1) if group_offsets is not None else S
+    _check(load().lora_attn_decode_noalloc(
+        _ptr(q), _ptr(k_base), _ptr(v_base), _ptr(block_tables), block_tables.shape[1], _ptr(context_lens),
+        max_context_len, _ptr(group_offsets), num_groups, _ptr(agent_ids), _ptr(adapter_start), _ptr(l_k_pools),
+        _ptr(l_v_pools), _ptr(b_k), _ptr(b_v), _ptr(ranks), max_rank, S, n_agents, Hq, Hkv, d, 16, sm_scale,
+        rope_theta, _dtype_code(q), _ptr(out), _stream(stream)))
 
 
 def lora_attn_prefill_workspace_size(S, Hq, Hkv, d, max_rank, max_q_len, max_context_len, dtype) -> int:

@@ -6,6 +6,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "../../include/lra.h"
 #include "internal.h"
 
@@ -345,7 +348,7 @@ int make_decode_args(DecodeArgs& a, DecodePlan& p, const void* q, const void* k_
                      const void* const* l_v_pools, const void* const* b_k, const void* const* b_v,
                      const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents, int32_t Hq, int32_t Hkv,
                      int32_t d, int32_t block_size, float sm_scale, float rope_theta, int32_t dtype, void* out,
-                     void* workspace, size_t workspace_bytes) {
+                     void* workspace, size_t workspace_bytes, bool fixed_scratch = false) {
   if (block_size != kBlock) return fail(LRA_ERR_UNSUPPORTED, "block_size must be 16 (got %d)", block_size);
   if (max_blocks < 1 || (long long)max_blocks * kBlock < max_context_len)
     return fail(LRA_ERR_INVALID_ARG, "max_blocks (%d) * 16 must cover max_context_len (%d)", max_blocks, max_context_len);
@@ -359,7 +362,9 @@ int make_decode_args(DecodeArgs& a, DecodePlan& p, const void* q, const void* k_
     return fail(LRA_ERR_INVALID_ARG, "sm_scale must be finite and rope_theta finite and >= 0");
   p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
   const size_t need = p.partial_bytes;
-  if (need && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+  // fixed_scratch: the records go to the library's fixed array, whose
+  // address the caller sets after these checks
+  if (need && !fixed_scratch && (!workspace || workspace_bytes < need || !aligned16(workspace)))
     return fail(LRA_ERR_WORKSPACE, "workspace of %zu bytes (16-byte aligned) needed (got %zu)", need, workspace_bytes);
   a.q = q;
   a.kb = k_base;
@@ -394,6 +399,94 @@ int make_decode_args(DecodeArgs& a, DecodePlan& p, const void* q, const void* k_
   a.rope = rope_theta > 0.f;
   rope_table(a.rope_rev, rope_theta, d);
   return LRA_OK;
+}
+
+// ---- allocation-free decode: the split records live in a fixed device array ----
+// Each GPU the library runs on holds its own copy of `scratch` until the
+// process ends. In host code the array's name is not a device address: the
+// address comes from hipGetSymbolAddress, taken once per device with that
+// device current, and only that address is passed to the kernels.
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The scratch address on the device of `stream` (taken on the first call
+// for that device).
+int scratch_of_stream(hipStream_t stream, void** out, const char* name) {
+  int dev = -1;
+  hipError_t e = stream ? hipStreamGetDevice(stream, &dev) : hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "%s: no device for the stream: %s", name, hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(LRA_ERR_UNSUPPORTED, "%s: device %d beyond %d", name, dev, kMaxDevices);
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_acquire);
+    if (!p) {
+      int cur = -1;
+      e = hipGetDevice(&cur);
+      if (e == hipSuccess && cur != dev) e = hipSetDevice(dev);
+      void* q = nullptr;
+      if (e == hipSuccess) e = hipGetSymbolAddress(&q, HIP_SYMBOL(scratch));
+      if (cur >= 0 && cur != dev) {
+        const hipError_t e2 = hipSetDevice(cur);
+        if (e == hipSuccess) e = e2;
+      }
+      if (e != hipSuccess || !q)
+        return fail(LRA_ERR_LAUNCH, "%s: address of the fixed scratch on device %d: %s", name, dev,
+                    hipGetErrorString(e));
+      g_scratch[dev].store(q, std::memory_order_release);
+      p = q;
+    }
+  }
+  *out = p;
+  return LRA_OK;
+}
+
+// The decode call, with a caller workspace or (noalloc) the fixed scratch.
+int decode_call(const char* name, const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
+                const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools,
+                const void* const* b_k, const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S,
+                int32_t N_agents, int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale,
+                float rope_theta, int32_t dtype, void* out, void* workspace, size_t workspace_bytes, bool noalloc,
+                void* stream) {
+  if (!group_offsets) num_groups = S;
+  int rc = check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+  if (rc != LRA_OK) return rc;
+  if (S == 0) return ok();
+  if (noalloc) {
+    // every host check first; the scratch address only once the call is valid
+    const DecodePlan p = decode_plan(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
+    if (p.partial_bytes > kNoAllocScratchBytes)
+      return fail(LRA_ERR_UNSUPPORTED,
+                  "%s: the split records of this call need %zu bytes, more than the fixed scratch of %zu bytes "
+                  "(use lora_attn_decode with a workspace)",
+                  name, p.partial_bytes, kNoAllocScratchBytes);
+  }
+  DecodeArgs a{};
+  DecodePlan p{};
+  rc = make_decode_args(a, p, q, k_base, v_base, block_tables, max_blocks, context_lens, max_context_len,
+                        group_offsets, num_groups, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks,
+                        max_rank, S, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out, workspace,
+                        workspace_bytes, noalloc);
+  if (rc != LRA_OK) return rc;
+  if (noalloc && p.partial_bytes) {
+    void* ptr = nullptr;
+    rc = scratch_of_stream((hipStream_t)stream, &ptr, name);
+    if (rc != LRA_OK) return rc;
+    a.partials = (float*)ptr;
+  }
+#ifdef LRA_DEBUG_CHECKS
+  rc = debug_check(decode_check_args(a, max_context_len, max_rank, N_agents, dtype), name, (hipStream_t)stream);
+  if (rc != LRA_OK) return rc;
+#endif
+  const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
+                                         : launch_decode_f32(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "%s launch failed: %s", name, hipGetErrorString(e));
+  return ok();
 }
 
 // Validation and arguments of the prefill kernel (sizes already checked,
@@ -541,26 +634,23 @@ int lora_attn_decode(const void* q, const void* k_base, const void* v_base, cons
                      const void* const* b_v, const int32_t* ranks, int32_t max_rank, int32_t S, int32_t N_agents,
                      int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size, float sm_scale, float rope_theta,
                      int32_t dtype, void* out, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!group_offsets) num_groups = S;
-  int rc = check_decode_sizes(S, num_groups, Hq, Hkv, d, max_rank, max_context_len, dtype);
-  if (rc != LRA_OK) return rc;
-  if (S == 0) return ok();
-  DecodeArgs a{};
-  DecodePlan p{};
-  rc = make_decode_args(a, p, q, k_base, v_base, block_tables, max_blocks, context_lens, max_context_len,
-                        group_offsets, num_groups, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks,
-                        max_rank, S, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out, workspace,
-                        workspace_bytes);
-  if (rc != LRA_OK) return rc;
-#ifdef LRA_DEBUG_CHECKS
-  rc = debug_check(decode_check_args(a, max_context_len, max_rank, N_agents, dtype), "lora_attn_decode",
-                   (hipStream_t)stream);
-  if (rc != LRA_OK) return rc;
-#endif
-  const hipError_t e = dtype == LRA_BF16 ? launch_decode_bf16(a, p.rp, p.na, (hipStream_t)stream)
-                                         : launch_decode_f32(a, (hipStream_t)stream);
-  if (e != hipSuccess) return fail(LRA_ERR_LAUNCH, "lora_attn_decode launch failed: %s", hipGetErrorString(e));
-  return ok();
+  return decode_call("lora_attn_decode", q, k_base, v_base, block_tables, max_blocks, context_lens, max_context_len,
+                     group_offsets, num_groups, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k, b_v, ranks, max_rank,
+                     S, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out, workspace, workspace_bytes,
+                     false, stream);
+}
+
+int lora_attn_decode_noalloc(const void* q, const void* k_base, const void* v_base, const int32_t* block_tables,
+                             int32_t max_blocks, const int32_t* context_lens, int32_t max_context_len,
+                             const int32_t* group_offsets, int32_t num_groups, const int32_t* agent_ids,
+                             const int32_t* adapter_start, const void* const* l_k_pools, const void* const* l_v_pools,
+                             const void* const* b_k, const void* const* b_v, const int32_t* ranks, int32_t max_rank,
+                             int32_t S, int32_t N_agents, int32_t Hq, int32_t Hkv, int32_t d, int32_t block_size,
+                             float sm_scale, float rope_theta, int32_t dtype, void* out, void* stream) {
+  return decode_call("lora_attn_decode_noalloc", q, k_base, v_base, block_tables, max_blocks, context_lens,
+                     max_context_len, group_offsets, num_groups, agent_ids, adapter_start, l_k_pools, l_v_pools, b_k,
+                     b_v, ranks, max_rank, S, N_agents, Hq, Hkv, d, block_size, sm_scale, rope_theta, dtype, out, nullptr,
+                     0, true, stream);
 }
 
 // --------------------------------------------------------------------------

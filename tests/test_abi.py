@@ -217,3 +217,22 @@ def test_debug_library_exports_and_validates_like_release():
         rc_d = dbg.lora_attn_decode(*args.values())
         assert rc_r == rc_d != 0, over
         assert lra.lra_last_error() == dbg.lra_last_error().decode(), over
+
+
+def test_decode_noalloc_rejects_before_any_hip_call():
+    """The allocation-free decode checks its arguments as lora_attn_decode
+    does, and rejects a call whose split records exceed its fixed 16 MiB
+    array, all before any HIP call (fake addresses are never touched)."""
+    lib = lra.load()
+    base = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, max_blocks=2048, ctx=FAKE, max_ctx=32768, go=None, ng=64, ag=FAKE,
+                act=None, lk=FAKE, lv=FAKE, bk=FAKE, bv=FAKE, ranks=FAKE, max_rank=64, S=64, NA=16, Hq=32, Hkv=8, d=128,
+                bs=16, sc=0.088, theta=5e5, dtype=lra.LRA_BF16, out=FAKE, stream=None)
+    call = lambda **o: (lib.lora_attn_decode_noalloc(*dict(base, **o).values()), lra.lra_last_error())  # noqa: E731
+    need = lra.lora_attn_decode_workspace_size(64, 64, 32, 8, 128, 64, 32768, lra.LRA_BF16)
+    assert need > 16 << 20
+    rc, msg = call()
+    assert rc == B.LRA_ERR_UNSUPPORTED and "fixed scratch" in msg, msg
+    rc, msg = call(q=None, S=4, ng=4, max_ctx=8192)
+    assert rc == B.LRA_ERR_INVALID_ARG and "null" in msg, msg
+    rc, msg = call(Hq=30, S=4, ng=4, max_ctx=8192)
+    assert rc == B.LRA_ERR_INVALID_ARG, msg
