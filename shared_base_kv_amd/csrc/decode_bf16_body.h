@@ -46,10 +46,16 @@ namespace dec {
 namespace {
 
 constexpr int D = 128;
-constexpr int kQPitch = D + 8;                    // LDS row pitch of the query tile (bf16)
+// LDS row pitches of the tiles that 16 rows read 16 bytes at a time: 72
+// dwords. A 16-byte LDS read serves lanes 0-7 with 16-23 (and so on) in one
+// pass, so the 8 rows of a pass must start 8 banks apart modulo 64: any odd
+// multiple of 8 dwords (measured on MI355X: no bank conflict at 72 dwords,
+// about 4 extra cycles per read at 68 and 36).
+constexpr int kQPitch = D + 16;                   // query tile (bf16)
 constexpr float kMaxSlack = 8.f;                  // log2 of the largest probability kept before a rescale
-constexpr int kRotPitch = kMaxRopePairs + 4;      // LDS row pitch of the per-column rotation table (f16 pairs)
-constexpr int kQpPitch = D + 8;                   // LDS row pitch of the permuted f16 query tile (halves)
+constexpr int kRotPitch = kMaxRopePairs + 8;      // per-column rotation table (f16 pairs)
+constexpr int kQpPitch = D + 16;                  // permuted f16 query tile (halves)
+
 
 struct TileAgent {
   const uint16_t* lk;
@@ -158,24 +164,6 @@ struct Cfg {
   static constexpr int kRegion = kBtBytes > kMergeBytes ? kBtBytes : kMergeBytes;
 };
 
-// LDS arrays of one workgroup (a kernel that runs this workgroup next to
-// another kind carves them from one buffer).
-template <int RP, int NA, bool KAD, bool VAD>
-struct Lds {
-  using C = Cfg<RP, NA, KAD, VAD>;
-  alignas(16) unsigned char s_region[C::kRegion];        // B_k^T [al][dim][k] in the loop, merge buffer after
-  alignas(16) uint16_t s_bvt[VAD ? NA * D * RP : 8];     // B_v^T [al][dim][k]
-  alignas(16) uint16_t s_q[16 * kQPitch];                // query tile [row][dim]
-  alignas(16) uint16_t s_qp[KAD ? 16 * kQpPitch : 8];    // f16 query tile, k slots of the adapter product
-  alignas(16) f16x2 s_roff[KAD ? 16 * kRotPitch : 4];    // (cos, sin) of lc theta_i, [lc][i]
-  alignas(16) f16x2 s_rbase[KAD ? kDecodeWaves : 1][kMaxRopePairs];  // per wave: (cos, sin) of tb theta_i
-  double s_rev[kMaxRopePairs];
-  TileAgent s_agent[NA];
-  float s_ml[2][C::HW][16];
-  int s_shared_l;
-  int s_lead;  // first agent slot of the tile with an adapter (its rows travel with the blocks)
-  int s_start_min, s_start_max;  // activation positions over the tile's adapted slots
-};
 
 }  // namespace
 }  // namespace dec

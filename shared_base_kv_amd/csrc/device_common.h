@@ -111,4 +111,24 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Offset of element (row, col) of a bf16 matrix of `nrows` rows and W
+// columns staged in LDS for MFMA operand reads, in which lane l reads row
+// l % 16 (plus a multiple of 16) at column group l / 16. Rows are not padded;
+// the pieces of a row are permuted by row bits so that one read instruction
+// hits distinct banks of the 64 (measured on MI355X):
+//   W = 16: 8-byte reads (4 columns per lane). A pass serves 32 lanes; rows 8
+//           apart share banks, so the second 8 rows take the other half of
+//           the row.
+//   W = 32 or 64: 16-byte reads (8 columns per lane). A pass serves lanes 0-7
+//           with 16-23 (and so on). The matrix is kept as W / 32 slabs of 32
+//           columns (so the slab of a read is an immediate offset), and rows
+//           4 apart, which share banks within a slab, take the other half of
+//           the row.
+template <int W>
+__device__ __forceinline__ int tile_off(int row, int col, int nrows) {
+  static_assert(W == 16 || W == 32 || W == 64, "tile width");
+  if constexpr (W == 16) return row * 16 + 4 * ((col >> 2) ^ (((row >> 3) & 1) << 1)) + (col & 3);
+  else return (col >> 5) * nrows * 32 + row * 32 + 8 * (((col >> 3) & 3) ^ (((row >> 2) & 1) << 1)) + (col & 7);
+}
+
 }  // namespace lra

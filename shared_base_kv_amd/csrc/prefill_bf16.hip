@@ -17,7 +17,7 @@ __global__ __launch_bounds__(pf::kThreads) void prefill_bf16_kernel(const Prefil
   __shared__ __align__(16) uint16_t s_k[kKBufs][kTile * kKPitch];           // rebuilt keys [key][dim]
   __shared__ __align__(16) uint16_t s_v[kVBufs][D * kVPitch];               // V^T [dim][key]
   __shared__ __align__(16) uint16_t s_lv[kVBufs][VAD ? RP * kVPitch : 8];   // L_v^T [rank][key]
-  __shared__ __align__(16) uint16_t s_bt[KAD ? D * RP : 8];                 // B_k^T [dim][rank]
+  __shared__ __align__(16) uint16_t s_bt[KAD ? D * RP : 8];                 // B_k^T [dim][rank] (see tile_off)
   __shared__ __align__(16) uint16_t s_bvt[VAD ? D * RP : 8];                // B_v^T [dim][rank]
   __shared__ __align__(16) float s_rot[kKBufs][2 * kMaxRopePairs];          // (cos, sin) of 64 t theta_i
   __shared__ double s_rev[kMaxRopePairs];

@@ -88,18 +88,6 @@ struct TileRegs {
   uint4 lvv[NPAR];             // L_v^T item lane + 64 u: rank item/2, keys 8 (item%2) .. +7
 };
 
-// LDS arrays of one workgroup (a kernel that runs this workgroup next to
-// another kind carves them from one buffer).
-template <int RP, bool KAD, bool VAD>
-struct Lds {
-  alignas(16) uint16_t s_k[kKBufs][kTile * kKPitch];          // rebuilt keys [key][dim]
-  alignas(16) uint16_t s_v[kVBufs][D * kVPitch];              // V^T [dim][key]
-  alignas(16) uint16_t s_lv[kVBufs][VAD ? RP * kVPitch : 8];  // L_v^T [rank][key]
-  alignas(16) uint16_t s_bt[KAD ? D * RP : 8];                // B_k^T [dim][rank]
-  alignas(16) uint16_t s_bvt[VAD ? D * RP : 8];               // B_v^T [dim][rank]
-  alignas(16) float s_rot[kKBufs][2 * kMaxRopePairs];         // (cos, sin) of 64 t theta_i
-  double s_rev[kMaxRopePairs];
-};
 
 }  // namespace
 }  // namespace pf
