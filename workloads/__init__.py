@@ -8,6 +8,7 @@ from .synth import (  # noqa: F401
     config_long_layer,
     config_mixed_step,
     config_prefill,
+    config_prefill_r64,
     config_serving_mix,
     config_tiny_f32,
     decode_workload,

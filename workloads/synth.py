@@ -416,6 +416,12 @@ def config_prefill(seed=0):
     return prefill_workload(name="8b_prefill_chunk", seed=seed)
 
 
+def config_prefill_r64(seed=0):
+    """The prefill chunk at rank 64 (shared-A r=64), the largest rank the
+    pages sweep."""
+    return prefill_workload(name="8b_prefill_chunk_r64", rank=64, seed=seed)
+
+
 def mixed_workload(
     name="mixed",
     dtype="bf16",
