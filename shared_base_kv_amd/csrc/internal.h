@@ -17,11 +17,9 @@ constexpr int kMaxSplits = 64;   // split-K partitions per (group, head, row til
 constexpr int kMaxTileAgents = 8;  // sequences of one decode row tile
 constexpr int kMaxRopePairs = 64;
 constexpr int kMaxSplitBlocks = 256;  // cache blocks in one split (split <= 4096 tokens)
-// 16-row tiles per prefill wave (8 waves per workgroup): two, or one at rank
-// 64 with both adapters
-constexpr int prefill_row_tiles(int rp, bool kad, bool vad) { return (rp == 64 && kad && vad) ? 1 : 2; }
-// query rows (tokens x query heads of one KV head) per prefill workgroup
-constexpr int prefill_rows(int rp, bool kad, bool vad) { return 8 * 16 * prefill_row_tiles(rp, kad, vad); }
+// query rows (tokens x query heads of one KV head) per prefill workgroup:
+// 8 waves of two 16-row tiles
+constexpr int kPrefillRows = 256;
 
 // Decode launch plan: derived on the host from sizes only, so the workspace
 // query and the launch agree.

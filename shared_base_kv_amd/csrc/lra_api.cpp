@@ -534,7 +534,7 @@ int make_prefill_args(PrefillArgs& a, const void* q, const void* k_base, const v
   a.G = Hq / Hkv;
   a.max_q_len = max_q_len;
   a.rp = pad_rank(max_rank);
-  a.q_tiles = ceil_div(max_q_len, prefill_rows(a.rp, b_k != nullptr, b_v != nullptr) / (Hq / Hkv));
+  a.q_tiles = ceil_div(max_q_len, kPrefillRows / (Hq / Hkv));
   a.sm_scale = sm_scale;
   a.sm_scale_log2 = (float)((double)sm_scale * 1.4426950408889634);
   a.rope = rope_theta > 0.f;

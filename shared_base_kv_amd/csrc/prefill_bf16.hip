@@ -16,9 +16,12 @@ __global__ __launch_bounds__(pf::kThreads) void prefill_bf16_kernel(const Prefil
   using namespace pf;
   __shared__ __align__(16) uint16_t s_k[kKBufs][kTile * kKPitch];           // rebuilt keys [key][dim]
   __shared__ __align__(16) uint16_t s_v[kVBufs][D * kVPitch];               // V^T [dim][key]
-  __shared__ __align__(16) uint16_t s_lv[kVBufs][VAD ? RP * kVPitch : 8];   // L_v^T [rank][key]
+  // rank space: L_v^T tiles [rank][key]; value rebuild: each wave's L_v rows [key][rank] (s_lvt)
+  __shared__ __align__(16) uint16_t s_lv[kVBufs][VAD ? RP * kVPitch : 8];
+  uint16_t* const s_lvt = &s_lv[0][0];
+  static_assert(!value_rebuild(RP, KAD, VAD) || 8 * kBlock * (RP + 8) <= kVBufs * RP * kVPitch, "L_v rows fit");
   __shared__ __align__(16) uint16_t s_bt[KAD ? D * RP : 8];                 // B_k^T [dim][rank] (see tile_off)
-  __shared__ __align__(16) uint16_t s_bvt[VAD ? D * RP : 8];                // B_v^T [dim][rank]
+  __shared__ __align__(16) uint16_t s_bvt[VAD ? D * RP : 8];                // B_v^T [dim][rank] (value rebuild: see tile_off)
   __shared__ __align__(16) float s_rot[kKBufs][2 * kMaxRopePairs];          // (cos, sin) of 64 t theta_i
   __shared__ double s_rev[kMaxRopePairs];
   const unsigned bid = blockIdx.x;

@@ -7,41 +7,41 @@
 // T - q_len + i and sees keys 0..position. Keys and values are the shared
 // base plus the agent's low-rank adapter part (LRAgent: Efficient KV Cache
 // Sharing for Multi-LoRA LLM Agents, abstract), and the adapter part is never
-// written to device memory at full dimension:
-//   - per 64-key tile the adapter key rope(L_k B_k) is rebuilt on MFMA,
-//     added to the base key and rounded once to bf16 into an LDS key tile;
-//   - values stay split: O accumulates P V_base, C accumulates P L_v in rank
-//     space, and C B_v is applied once per row after the key loop.
+// written to device memory at full dimension: per 64-key tile the adapter
+// key rope(L_k B_k) and the adapter value L_v B_v are rebuilt on MFMA, added
+// to the base key and value and rounded once to bf16 into the LDS tiles.
+// (The decode kernel keeps values in rank space, P L_v and then B_v once per
+// row. A prefill workgroup has 256 query rows per KV head, twice the head
+// dimension, so rebuilding a tile's 64 values takes half the products of
+// 256 rows of P L_v, and no rank-space accumulator takes registers.)
 //
 // Work decomposition: one workgroup = (sequence s, KV head h, query tile);
-// a query tile has 256 rows = 256/G query tokens x G query heads (128 rows at
-// rank 64 with both adapters, whose rank-space accumulators would not fit the
-// registers beside two row tiles). Each of the 8 waves (two per SIMD)
-// consumes 32 (16) query rows (scores, softmax, P V on the
-// matrix cores) and also produces part of the next tile: with a key adapter
-// every wave loads and rebuilds half of one 16-key cache block (half of the
-// rotary pairs and of the V^T rows), so the rebuild's registers fit beside
-// the consumer's; without one, waves 0..3 each copy a whole block. Two
-// consumers per SIMD let one wave's softmax, rebuild and LDS waits run under
-// the other's matrix work. All tiles of one KV head are dealt to one XCD, so
-// the keys they share (the common prefix) stream through one L2.
+// a query tile has 256 rows = 256/G query tokens x G query heads. Each of
+// the 8 waves (two per SIMD) consumes 32 query rows (scores, softmax, P V on
+// the matrix cores) and also produces part of the next tile: with a key
+// adapter every wave loads and rebuilds half of one 16-key cache block (half
+// of the rotary pairs and of the value dims), so the rebuild's registers fit
+// beside the consumer's; without one, waves 0..3 each take a whole block.
+// Two consumers per SIMD let one wave's softmax, rebuild and LDS waits run
+// under the other's matrix work. All tiles of one KV head are dealt to one
+// XCD, so the keys they share (the common prefix) stream through one L2.
 //
 // Matrix-core mapping (16x16 tiles):
-//   X^T[dim, key]   = B_k^T L_k^T        (per producer: its block's keys, 16x16x16 / 16x16x32)
+//   X^T[dim, key]   = B_k^T L_k^T        (producer: its block's keys, 16x16x16 / 16x16x32)
+//   V_a[key, dim]   = V + L_v B_v        (producer: V in the accumulator; L_v turned to
+//                                         [key][rank] through the wave's own LDS rows)
 //   S^T[key, row]   = K_a Q^T            (16x16x32, K_a from LDS)
-//   O^T[dim, row]  += V^T P^T            (16x16x32, V^T from LDS, P^T from the S^T accumulators)
-//   C^T[rank, row] += L_v^T P^T
-//   O^T            += B_v^T C^T          (after the loop; C split into bf16 hi + lo)
+//   O^T[dim, row]  += V_a^T P^T          (16x16x32, V_a^T from LDS, P^T from the S^T accumulators)
 //
 // Pipeline (one barrier per tile): in step t each wave issues the scores of
 // tile t and P V of tile t-1 together, runs the softmax of tile t while the
 // matrix cores work through them, then rebuilds its part of tile t+1 into
 // the other LDS buffers and issues the loads of tile t+2. Keys are
-// double-buffered in LDS and V^T, L_v^T triple-buffered (tile t-1 is read
-// while t+1 is written). The rotation of
-// the adapter key at position 64t + o is split by angle addition into a
-// per-tile part (64t, one table of 64 pairs per tile) and a per-lane part (o,
-// fixed for the whole loop), so no transcendental is evaluated per element.
+// double-buffered in LDS and V^T triple-buffered (tile t-1 is read while
+// t+1 is written). The rotation of the adapter key at position 64t + o is
+// split by angle addition into a per-tile part (64t, one table of 64 pairs
+// per tile) and a per-lane part (o, fixed for the whole loop), so no
+// transcendental is evaluated per element.
 #pragma once
 #include <type_traits>
 
@@ -55,7 +55,7 @@ namespace {
 constexpr int D = 128;
 constexpr int kTile = 64;      // keys per tile (4 cache blocks)
 constexpr int kKPitch = D + 16;         // LDS row pitch of the key tile (bf16; 72 dwords: 16-byte reads conflict-free)
-constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T / L_v^T tiles (bf16)
+constexpr int kVPitch = kTile + 8;      // LDS row pitch of the V^T tile (bf16)
 constexpr int kKBufs = 2;
 constexpr int kVBufs = 3;
 constexpr int kThreads = 512;  // 8 waves of 32 query rows
@@ -75,17 +75,37 @@ __device__ __forceinline__ float2 cos_sin_rev(double x) {
   return make_float2(__builtin_amdgcn_cosf(f), __builtin_amdgcn_sinf(f));
 }
 
+// Values: rank space (O accumulates P V_base, C accumulates P L_v, C B_v
+// once per row after the key loop) except at rank 64 with both adapters,
+// where the two rank-space row tiles of a wave do not fit the registers
+// beside the key rebuild: there the producers rebuild the values as
+// V + L_v B_v into the V^T tile instead (measured: 0.905 -> 0.612 ms for the
+// 4 x 512-token chunk at rank 64; at ranks 16 and 32, and with a value
+// adapter alone, the rank-space form is 2-25% faster).
+constexpr bool value_rebuild(int rp, bool kad, bool vad) { return rp == 64 && kad && vad; }
+
+// v, made opaque to the compiler when ON (so that values derived from it are
+// recomputed where they are used rather than kept in registers).
+template <bool ON>
+__device__ __forceinline__ int opaque_if(int v) {
+  if constexpr (ON) asm volatile("" : "+v"(v));
+  return v;
+}
+
 // One producer wave's share of a 16-key cache block of a tile, on its way
 // from HBM: the whole block (NH = 1) or half of it (NH = 2: rotary pairs
-// 32 hh .. 32 hh + 31 and the V^T rows of parity hh).
-template <int RP, int NH>
+// 32 hh .. 32 hh + 31, and the V^T rows of parity hh in rank space or value
+// dims 64 hh .. 64 hh + 63 in the value rebuild).
+template <int RP, int NH, bool VREB>
 struct TileRegs {
   static constexpr int NCB = 4 / NH;  // 16-pair groups cb
-  static constexpr int NPAR = 2 / NH; // V^T row parities
-  uint2 kbl[NCB], kbh[NCB];    // base keys of key lc: dims 16cb + 4lg .. +3 and +64
-  uint4 vv[NPAR][2];           // V^T row 2 lane + parity, keys 8k .. +7 of the block (k = 0, 1)
-  uint4 lk[RP == 64 ? 2 : 1];  // L_k row of key lc: ranks 8lg.. (RP 32/64) or 4lg.. (RP 16, .x .y)
-  uint4 lvv[NPAR];             // L_v^T item lane + 64 u: rank item/2, keys 8 (item%2) .. +7
+  static constexpr int NPAR = 2 / NH; // V^T row parities (rank space)
+  static constexpr int NDT = 8 / NH;  // 16-dim value tiles (value rebuild)
+  uint2 kbl[NCB], kbh[NCB];     // base keys of key lc: dims 16cb + 4lg .. +3 and +64
+  uint4 vv[VREB ? 1 : NPAR][2]; // rank space: V^T row 2 lane + parity, keys 8k .. +7 of the block (k = 0, 1)
+  uint2 vb[VREB ? NDT : 1];     // value rebuild: base values of dim 16dt + lc, keys 4lg .. +3 of the block
+  uint4 lk[RP == 64 ? 2 : 1];   // L_k row of key lc: ranks 8lg.. (RP 32/64) or 4lg.. (RP 16, .x .y)
+  uint4 lvv[VREB ? (RP == 64 ? 2 : 1) : NPAR];  // L_v^T item lane + 64 u: rank item/2, keys 8 (item%2) .. +7
 };
 
 
