@@ -40,7 +40,7 @@ SMALL = [
     (32, 8, (2, 1, 3), (129, 16, 700), (16,) * 6, True, 1e4),
     (16, 8, (8,), (300,), (32,) * 8, False, 5e5),  # G=2, 8 agents/tile
     (8, 8, (5,), (77,), (8,) * 5, False, 5e5),  # G=1
-    (8, 8, (12,), (300,), (16,) * 12, False, 5e5),  # G=1, 12 agents in one tile (16-agent variant)
+    (8, 8, (12,), (300,), (16,) * 12, False, 5e5),  # G=1, 12 agents: row tiles of 8 and 4 over one base
     (32, 8, (3,), (400,), (16, 32, 8), False, 5e5),  # separate pools of different ranks in one tile
     (64, 8, (3,), (260,), (64,) * 3, False, 5e5),  # G=8: 2 agents per tile -> 2 row tiles
     (128, 8, (2,), (200,), (16, 16), False, 5e5),  # G=16: 1 agent per tile
