@@ -135,6 +135,7 @@ PREFILL = [
     (32, 8, 32, (70,), 64, None),
     (16, 8, 16, (90, 5), 16, (1, -1)),
     (32, 8, 256, (200, 31, 9), 16, (-1, 0, 2)),
+    (32, 8, 48, (70, 33), 64, (-1, 1)),  # rank 64: values rebuilt in the kernel, one sequence agent-less
 ]
 
 

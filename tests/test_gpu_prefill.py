@@ -9,7 +9,7 @@ import torch
 import oracle
 import shared_base_kv_amd as lra
 from tests.gpu_harness import TOL_BF16, oracle_rows, row_rel_err, run_prefill, to_np, upload
-from workloads import BLOCK, bf16_bits, build_inputs, config_prefill, prefill_workload
+from workloads import BLOCK, bf16_bits, build_inputs, config_prefill, config_prefill_r64, prefill_workload
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,18 @@ def test_prefill_chunk_full_size_sampled_rows():
     for s in range(w.S):
         base = [0, 1, 31, 32, 33, 255, 256, 510, 511]
         picks[s] = sorted(set(base + rng.choice(512, 31, replace=False).tolist()))
+    _check(w, q_rows=picks)
+
+
+def test_prefill_chunk_rank64_full_size_sampled_rows():
+    """The same chunk at rank 64, where the kernel rebuilds the values in LDS
+    instead of accumulating P L_v; 20 rows per agent."""
+    w = config_prefill_r64()
+    rng = np.random.default_rng(4)
+    picks = {}
+    for s in range(w.S):
+        base = [0, 63, 64, 255, 256, 511]
+        picks[s] = sorted(set(base + rng.choice(512, 14, replace=False).tolist()))
     _check(w, q_rows=picks)
 
 
