@@ -419,9 +419,9 @@ def leg_prefill_absent(K, W, adapt, starts=None, config=None):
 
 def leg_varlen(K, W):
     """One serving step of the 8B-shaped layer (the 4-agent decode on its
-    8192-token base plus the 4 x 512-token prefill chunk): lora_attn_varlen
-    (one grid) against lora_attn_decode followed by lora_attn_prefill, with
-    the same context and query-length bounds."""
+    8192-token base plus the 4 x 512-token prefill chunk): one
+    lora_attn_varlen call against lora_attn_decode followed by
+    lora_attn_prefill, with the same context and query-length bounds."""
     import torch
 
     import shared_base_kv_amd as lra

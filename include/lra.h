@@ -264,8 +264,13 @@ int lora_attn_decode_noalloc(const void* q, const void* k_base, const void* v_ba
  *   max_q_len     (host) >= every q_len_s.
  *   Everything else as for decode (no grouping; agent id -1, adapter_start
  *   and NULL b_k / b_v as there: without a key adapter the key tiles are the
- *   base keys as stored, without a value adapter no rank-space accumulator is
- *   kept; key tiles wholly before the activation point skip the rebuild).
+ *   base keys as stored, without a value adapter the value tiles are the base
+ *   values; key tiles wholly before the activation point read no low-rank
+ *   rows). With a value adapter the values are kept in rank space (P L_v,
+ *   then B_v once per row), except at rank 64 with both adapters, where each
+ *   64-key tile's values are rebuilt as V + L_v B_v in LDS and rounded once
+ *   to bf16, like the keys; either way nothing of full dimension is written
+ *   to device memory.
  *   dtype: LRA_BF16, d = 128.
  *   workspace     lora_attn_prefill_workspace_size(...) bytes (may be 0,
  *                 then workspace may be NULL).
