@@ -374,7 +374,7 @@ def leg_prefill(K, W):
 
     def build_all():
         for a in range(4):
-            lra.lr_cache_build(Xs[a], Ak, dw.lk_pools[0], bws, slot_mapping=slots[a], l_layout=lra.LRA_L_TOKEN_MAJOR,
+            lra.lr_cache_build(Xs[a], Ak, dw.lk_pools[0], bws, slot_mapping=slots[a], l_layout=lra.LRA_L_KEY_CHUNKED,
                                ldl=16)
             lra.lr_cache_build(Xs[a], Av, dw.lv_pools[0], bws, slot_mapping=slots[a], l_layout=lra.LRA_L_RANK_MAJOR)
 
@@ -501,9 +501,9 @@ def leg_lr_multi(K, W, n_agents=4, rank=16):
     nb = n // 16 + 8
     slots = torch.randperm(nb * 16, generator=torch.Generator().manual_seed(1))[:n].cuda()
     cols = [rank * g for g in range(2 * n_agents + 1)]
-    lays = [lra.LRA_L_TOKEN_MAJOR, lra.LRA_L_RANK_MAJOR] * n_agents
-    pools = [torch.zeros((nb, 16, rank) if l == 0 else (nb, rank, 16), dtype=torch.bfloat16, device="cuda")
-             for l in lays]
+    lays = [lra.LRA_L_KEY_CHUNKED, lra.LRA_L_RANK_MAJOR] * n_agents
+    pools = [torch.zeros((nb, rank // 8, 16, 8) if l == lra.LRA_L_KEY_CHUNKED else (nb, rank, 16),
+                         dtype=torch.bfloat16, device="cuda") for l in lays]
     ws = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, ncols), dtype=torch.uint8, device="cuda")
     ws1 = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, rank), dtype=torch.uint8, device="cuda")
 

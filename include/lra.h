@@ -34,7 +34,7 @@
  *   sequence, the context length (1..max_context_len), the block ids of the
  *   used table entries (>= 0; the pool size is not passed, so not the upper
  *   bound), the agent id (-1..N_agents-1), that agent's rank
- *   (1..max_rank, a multiple of 8 with LRA_BF16) and pool / B pointers,
+ *   (1..max_rank, a multiple of 8) and pool / B pointers,
  *   adapter_start (>= 0), the query count (0..min(max_q_len, context
  *   length)), the decode rows of a varlen call (cu_q_lens[s] = s for
  *   s <= S_dec), and that group_offsets rise
@@ -50,7 +50,9 @@
  * Cache layout (block size 16 tokens, NB physical blocks):
  *   k_base   [NB, Hkv, 16, d]   keys of one (block, head), token-major
  *   v_base   [NB, Hkv, d, 16]   values of one (block, head), 16 tokens of a dim contiguous
- *   L_k pool [NB, 16, r]        token-major low-rank key rows
+ *   L_k pool [NB, r/8, 16, 8]   low-rank key rows in chunks of 8 ranks: rank j of
+ *                               slot t at ((j/8)*16 + t)*8 + j%8 within the block
+ *                               (ranks 8q..8q+7 of all 16 slots are one contiguous run)
  *   L_v pool [NB, r, 16]        rank-major low-rank value rows
  *   B_k, B_v [r, Hkv*d]         per agent; column h*d + i feeds KV head h, dim i
  * A sequence's token n lives in physical block block_tables[s][n/16], slot
@@ -83,8 +85,10 @@ typedef enum lra_dtype { LRA_F32 = 0, LRA_BF16 = 1 } lra_dtype;
 
 /* Where lr_cache_build stores rows when a slot mapping is given. */
 typedef enum lra_l_layout {
-  LRA_L_TOKEN_MAJOR = 0, /* pool [NB, 16, ldl]: row of slot s at L + s*ldl (the L_k layout) */
-  LRA_L_RANK_MAJOR = 1   /* pool [NB, n_cols, 16]: column c of slot s at L + ((s/16)*n_cols + c)*16 + s%16 (the L_v layout) */
+  LRA_L_TOKEN_MAJOR = 0, /* pool [NB, 16, ldl]: row of slot s at L + s*ldl (a plain paged row store) */
+  LRA_L_RANK_MAJOR = 1,  /* pool [NB, n_cols, 16]: column c of slot s at L + ((s/16)*n_cols + c)*16 + s%16 (the L_v layout) */
+  LRA_L_KEY_CHUNKED = 2  /* pool [NB, n_cols/8, 16, 8]: column c of slot s at
+                            L + (s/16)*16*n_cols + ((c/8)*16 + s%16)*8 + c%8 (the L_k layout; n_cols % 8 == 0) */
 } lra_l_layout;
 
 /* LRA_VERSION of the built library. */
@@ -134,7 +138,8 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
  * [group_cols[g], group_cols[g+1]) form group g (say agent a's A_k, then its
  * A_v), of width r_g. Row i of X A, restricted to group g, goes to slot
  * slot_mapping[i] of the pool group_pools[g], laid out as group_layouts[g]
- * says with n_cols = r_g (token-major [NB,16,r_g] or rank-major [NB,r_g,16]);
+ * says with n_cols = r_g (token-major [NB,16,r_g], rank-major [NB,r_g,16] or
+ * key-chunked [NB,r_g/8,16,8]);
  * a negative slot skips the row. Every column of X A is formed exactly as
  * lr_cache_build forms it (same sums in the same order), so each group's
  * rows are bit-identical to a separate lr_cache_build of that group, while X
@@ -195,8 +200,8 @@ int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda,
  *                 for values (V = V_base, l_v_pools not read). Both NULL:
  *                 plain attention over the base cache; agent_ids, ranks and
  *                 N_agents are not read and max_rank must be 0.
- *   ranks         int32 [N_agents], each in 1..max_rank; with LRA_BF16 each
- *                 rank must be a multiple of 8 (rows are read 16 bytes at a time).
+ *   ranks         int32 [N_agents], each in 1..max_rank and a multiple of 8
+ *                 (the L_k pool holds chunks of 8 ranks).
  *   max_rank      (host) 1..64, or 0 without adapters (pass the same value to
  *                 the workspace query). d: 64 or 128 (bf16: 128). block_size: 16.
  *   sm_scale      softmax scale (usually 1/sqrt(d)).

@@ -7,6 +7,7 @@ from .binding import (  # noqa: F401
     EXPORTS,
     LRA_BF16,
     LRA_F32,
+    LRA_L_KEY_CHUNKED,
     LRA_L_RANK_MAJOR,
     LRA_L_TOKEN_MAJOR,
     LraError,

@@ -25,6 +25,7 @@ LRA_F32 = 0
 LRA_BF16 = 1
 LRA_L_TOKEN_MAJOR = 0
 LRA_L_RANK_MAJOR = 1
+LRA_L_KEY_CHUNKED = 2
 
 EXPORTS = (
     "lra_version",

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
         const int phys = sPhys[t / kBlock], slot = n % kBlock;
         float x1 = 0.f, x2 = 0.f;
         for (int k = 0; k < (n >= act ? rk : 0); ++k) {
-          const float l = lk[((size_t)phys * kBlock + slot) * rk + k];
+          const float l = lk[(size_t)phys * kBlock * rk + ((k >> 3) * kBlock + slot) * 8 + (k & 7)];
           x1 = fmaf(l, bk[(size_t)k * HD + h * D + i], x1);
           x2 = fmaf(l, bk[(size_t)k * HD + h * D + i + HALF], x2);
         }

@@ -83,6 +83,17 @@ __device__ __forceinline__ uint2 bld8(__amdgpu_buffer_rsrc_t r, int byte_off) {
 }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
+// Byte offsets, within one cache block of an L_k pool, of the low-rank key
+// row pieces a matrix operand takes. The pool keeps chunks of 8 ranks: rank j
+// of token t at ((j/8)*16 + t)*8 + j%8, so the 16 tokens' rows of one chunk
+// are one contiguous 256-byte run and a wave's load of 16-byte pieces reads
+// whole runs (measured on MI355X: a quarter-wave reading 16 rows 128 bytes
+// apart moves L2-resident data 2.6 times slower).
+//   16-byte piece: ranks 32kc + 8g .. +7 of token t
+__device__ __forceinline__ int lk_chunk_off32(int t, int g, int kc) { return ((4 * kc + g) * 16 + t) * 16; }
+//   8-byte piece: ranks 4g .. 4g+3 of token t
+__device__ __forceinline__ int lk_chunk_off16(int t, int g) { return (((g >> 1) * 16 + t) * 8 + 4 * (g & 1)) * 2; }
+
 // Load of a value that is the same for the whole wave from memory the kernel
 // never writes: read through the constant address space, so a wave-uniform
 // address becomes a scalar load (counted apart from the vector loads in

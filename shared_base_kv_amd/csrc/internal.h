@@ -86,7 +86,7 @@ struct BuildArgs {
   int32_t row_tiles, col_tiles;
   int32_t n_groups;
   int32_t group_col[kMaxBuildGroups + 1];
-  int32_t group_layout[kMaxBuildGroups];  // 0 token-major (row stride group_ld), 1 rank-major
+  int32_t group_layout[kMaxBuildGroups];  // 0 token-major (row stride group_ld), 1 rank-major, 2 key-chunked
   int64_t group_ld[kMaxBuildGroups];
   void* group_dst[kMaxBuildGroups];
   int32_t ksplit;     // slices of the hidden dimension (ceil(hidden / kBuildSlice))

@@ -17,8 +17,8 @@
 // to the workspace and takes a ticket from the tile's counter; the workgroup
 // that arrives last adds the partials in slice order (so the result does not
 // depend on the arrival order), rounds once to bf16, stores densely or
-// through the slot mapping into the destination group's token-major or
-// rank-major paged pool, and puts the counter back to zero. The column tiles
+// through the slot mapping into the destination group's token-major,
+// rank-major or key-chunked paged pool, and puts the counter back to zero. The column tiles
 // of one (row tile, slice) are consecutive work items dealt to one XCD, so
 // the X rows they share are read into that L2 once.
 //
@@ -197,8 +197,10 @@ __global__ __launch_bounds__(kBuildThreads) void lr_build_kernel(const BuildArgs
     else if (slot >= 0) {
       if (a.group_layout[g] == 0)
         L[(size_t)slot * ld + c] = b;
-      else
+      else if (a.group_layout[g] == 1)
         L[((size_t)(slot / kBlock) * w + c) * kBlock + (slot % kBlock)] = b;
+      else
+        L[(size_t)(slot / kBlock) * kBlock * w + ((c / 8) * kBlock + slot % kBlock) * 8 + c % 8] = b;
     }
   }
 }

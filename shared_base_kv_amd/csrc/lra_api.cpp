@@ -132,7 +132,7 @@ struct CheckArgs {
   const void* const* bk;
   const void* const* bv;
   int32_t max_blocks, max_context_len, max_q_len, max_rank, S, num_groups, N_agents;
-  int32_t dtype;  // LRA_BF16: ranks must be multiples of 8 (low-rank rows are read 16 bytes at a time)
+  int32_t dtype;  // element type of the call
 };
 
 // in the order of report priority (per-sequence checks before group checks)
@@ -154,7 +154,7 @@ const char* check_message(int code) {
     case kChkContext: return "context length outside 1..max_context_len";
     case kChkBlock: return "negative physical block id in a used block-table entry";
     case kChkAgent: return "agent id outside -1..N_agents-1";
-    case kChkRank: return "agent rank outside 1..max_rank, or not a multiple of 8 with LRA_BF16";
+    case kChkRank: return "agent rank outside 1..max_rank, or not a multiple of 8";
     case kChkPool: return "null low-rank pool or B pointer for an agent in use";
     case kChkStart: return "negative adapter_start";
     case kChkGroups: return "group_offsets do not rise strictly from 0 to S";
@@ -186,7 +186,7 @@ __global__ void check_inputs_kernel(const CheckArgs c) {
     if (ag < -1 || ag >= c.N_agents) return report(kChkAgent, s);
     if (ag >= 0) {
       const int r = c.ranks[ag];
-      if (r < 1 || r > c.max_rank || (c.dtype == LRA_BF16 && r % 8 != 0)) return report(kChkRank, s);
+      if (r < 1 || r > c.max_rank || r % 8 != 0) return report(kChkRank, s);
       if ((c.bk && (!c.bk[ag] || !c.lk[ag])) || (c.bv && (!c.bv[ag] || !c.lv[ag]))) return report(kChkPool, s);
     }
     if (c.act && c.act[s] < 0) return report(kChkStart, s);
@@ -555,10 +555,12 @@ int lr_cache_build(const void* X, int64_t ldx, const void* A, int64_t lda, void*
   if (rc != LRA_OK) return rc;
   if (n_tokens == 0) return ok();
   if (!L) return fail(LRA_ERR_INVALID_ARG, "lr_cache_build: L must be non-null");
-  if (l_layout != LRA_L_TOKEN_MAJOR && l_layout != LRA_L_RANK_MAJOR)
+  if (l_layout != LRA_L_TOKEN_MAJOR && l_layout != LRA_L_RANK_MAJOR && l_layout != LRA_L_KEY_CHUNKED)
     return fail(LRA_ERR_INVALID_ARG, "unknown l_layout %d", l_layout);
   if (!slot_mapping && l_layout != LRA_L_TOKEN_MAJOR)
     return fail(LRA_ERR_INVALID_ARG, "a dense store (no slot mapping) is token-major only");
+  if (l_layout == LRA_L_KEY_CHUNKED && n_cols % 8)
+    return fail(LRA_ERR_INVALID_ARG, "a key-chunked pool needs n_cols %% 8 == 0 (got %d)", n_cols);
   if (l_layout == LRA_L_TOKEN_MAJOR && ldl < n_cols)
     return fail(LRA_ERR_INVALID_ARG, "ldl (%lld) < n_cols (%d)", (long long)ldl, n_cols);
   BuildArgs a{};
@@ -596,8 +598,11 @@ int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda,
     if (group_cols[g + 1] <= group_cols[g])
       return fail(LRA_ERR_INVALID_ARG, "group %d is empty or group_cols is not increasing", g);
     if (!group_pools[g]) return fail(LRA_ERR_INVALID_ARG, "group_pools[%d] is null", g);
-    if (group_layouts[g] != LRA_L_TOKEN_MAJOR && group_layouts[g] != LRA_L_RANK_MAJOR)
+    if (group_layouts[g] != LRA_L_TOKEN_MAJOR && group_layouts[g] != LRA_L_RANK_MAJOR &&
+        group_layouts[g] != LRA_L_KEY_CHUNKED)
       return fail(LRA_ERR_INVALID_ARG, "group_layouts[%d] = %d is not a layout", g, group_layouts[g]);
+    if (group_layouts[g] == LRA_L_KEY_CHUNKED && (group_cols[g + 1] - group_cols[g]) % 8)
+      return fail(LRA_ERR_INVALID_ARG, "group %d: a key-chunked pool needs a width that is a multiple of 8", g);
   }
   if (!slot_mapping) return fail(LRA_ERR_INVALID_ARG, "lr_cache_build_multi needs a slot mapping");
   if (n_tokens == 0) return ok();

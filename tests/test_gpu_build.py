@@ -65,16 +65,20 @@ def test_build_paged_stores_bit_exact():
     _build(X, A, L=tok, slot_mapping=sm, l_layout=lra.LRA_L_TOKEN_MAJOR, ldl=r)
     rk = torch.zeros((nb, r, 16), dtype=torch.bfloat16, device="cuda")
     _build(X, A, L=rk, slot_mapping=sm, l_layout=lra.LRA_L_RANK_MAJOR)
+    ch = torch.zeros((nb, r // 8, 16, 8), dtype=torch.bfloat16, device="cuda")
+    _build(X, A, L=ch, slot_mapping=sm, l_layout=lra.LRA_L_KEY_CHUNKED)
     d = dense.view(torch.int16).cpu().numpy()
     t = tok.view(torch.int16).cpu().numpy().reshape(nb * 16, r)
     k = rk.view(torch.int16).cpu().numpy().transpose(0, 2, 1).reshape(nb * 16, r)
+    # key-chunked: rank j of slot s at block s/16, ((j/8)*16 + s%16)*8 + j%8
+    c = ch.view(torch.int16).cpu().numpy().transpose(0, 2, 1, 3).reshape(nb * 16, r)
     for i, s in enumerate(slots):
         if s < 0:
             continue
-        assert np.array_equal(t[s], d[i]) and np.array_equal(k[s], d[i])
+        assert np.array_equal(t[s], d[i]) and np.array_equal(k[s], d[i]) and np.array_equal(c[s], d[i])
     written = set(int(s) for s in slots if s >= 0)
     untouched = [s for s in range(nb * 16) if s not in written]
-    assert not t[untouched].any() and not k[untouched].any()
+    assert not t[untouched].any() and not k[untouched].any() and not c[untouched].any()
 
 
 def _multi_case(n, hidden, ranks, seed):
@@ -82,7 +86,7 @@ def _multi_case(n, hidden, ranks, seed):
     widths = [r for r in ranks for _ in (0, 1)]  # agent a: A_k then A_v
     cols = np.concatenate([[0], np.cumsum(widths)]).astype(np.int32).tolist()
     X, A = build_inputs(n, hidden, cols[-1], seed=seed)
-    lays = [lra.LRA_L_TOKEN_MAJOR, lra.LRA_L_RANK_MAJOR] * len(ranks)
+    lays = [lra.LRA_L_KEY_CHUNKED, lra.LRA_L_RANK_MAJOR] * len(ranks)
     return X, A, cols, lays, widths
 
 
@@ -102,8 +106,8 @@ def test_multi_build_equals_single_builds_bit_exact(shape):
     Xd, Ad = _dev_bf16(X), _dev_bf16(A)
 
     def pools():
-        return [torch.zeros((nb, 16, w) if lay == 0 else (nb, w, 16), dtype=torch.bfloat16, device="cuda")
-                for w, lay in zip(widths, lays)]
+        return [torch.zeros((nb, w // 8, 16, 8) if lay == lra.LRA_L_KEY_CHUNKED else (nb, w, 16),
+                            dtype=torch.bfloat16, device="cuda") for w, lay in zip(widths, lays)]
 
     multi = pools()
     ws = torch.zeros(lra.lr_cache_build_workspace_size(n, hidden, cols[-1]), dtype=torch.uint8, device="cuda")
@@ -118,9 +122,14 @@ def test_multi_build_equals_single_builds_bit_exact(shape):
     for g, (w, lay) in enumerate(zip(widths, lays)):
         m = multi[g].view(torch.int16).cpu().numpy()
         assert np.array_equal(m, single[g].view(torch.int16).cpu().numpy()), g
-        rows = m.reshape(nb * 16, w) if lay == 0 else m.transpose(0, 2, 1).reshape(nb * 16, w)
-        got = multi[g].float().cpu().numpy()
-        got = got.reshape(nb * 16, w) if lay == 0 else got.transpose(0, 2, 1).reshape(nb * 16, w)
+
+        def rows_of(x):
+            if lay == lra.LRA_L_KEY_CHUNKED:
+                return x.transpose(0, 2, 1, 3).reshape(nb * 16, w)
+            return x.transpose(0, 2, 1).reshape(nb * 16, w)
+
+        rows = rows_of(m)
+        got = rows_of(multi[g].float().cpu().numpy())
         keep = slots >= 0
         assert row_rel_err(got[slots[keep]], refs[g][keep]) <= TOL_BF16, g
         untouched = sorted(set(range(nb * 16)) - set(int(s) for s in slots[keep]))

@@ -108,7 +108,7 @@ def test_prefill_matches_decode_rows():
 
 def test_build_then_prefill_pipeline():
     """The low-rank rows of each agent's new tokens are produced on the GPU by
-    lr_cache_build (X_a A_k into the token-major L_k pool, X_a A_v into the
+    lr_cache_build (X_a A_k into the key-chunked L_k pool, X_a A_v into the
     rank-major L_v pool) and then read by the prefill kernel. The oracle runs
     the same pipeline in fp64 with L = X_a A unrounded."""
     w = prefill_workload(name="pipe", prefix=64, q_lens=(48, 29), rank=16, seed=40)
@@ -123,7 +123,7 @@ def test_build_then_prefill_pipeline():
         slots = (seg.blocks.astype(np.int64)[:, None] * BLOCK + np.arange(BLOCK)[None, :]).reshape(-1)[: seg.T]
         sm = torch.from_numpy(slots).cuda()
         ws = torch.zeros(lra.lr_cache_build_workspace_size(seg.T, hidden, 16), dtype=torch.uint8, device="cuda")
-        lra.lr_cache_build(dev(Xs[a]), dev(Ak), dw.lk_pools[0], ws, slot_mapping=sm, l_layout=lra.LRA_L_TOKEN_MAJOR,
+        lra.lr_cache_build(dev(Xs[a]), dev(Ak), dw.lk_pools[0], ws, slot_mapping=sm, l_layout=lra.LRA_L_KEY_CHUNKED,
                            ldl=16)
         lra.lr_cache_build(dev(Xs[a]), dev(Av), dw.lv_pools[0], ws, slot_mapping=sm, l_layout=lra.LRA_L_RANK_MAJOR)
     got = to_np(run_prefill(dw))

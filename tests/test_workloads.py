@@ -32,7 +32,7 @@ def _gather_check(w, poison):
         k = to32(kpool[ids]).transpose(0, 2, 1, 3).reshape(nblk * BLOCK, w.Hkv, w.d)[:T]
         v = to32(vpool[ids]).transpose(0, 3, 1, 2).reshape(nblk * BLOCK, w.Hkv, w.d)[:T]
         p = w.pool_of_agent[w.seqs[s].agent]
-        lk = to32(lkp[p][ids]).reshape(nblk * BLOCK, -1)[:T]
+        lk = to32(lkp[p][ids]).transpose(0, 2, 1, 3).reshape(nblk * BLOCK, -1)[:T]
         lv = to32(lvp[p][ids]).transpose(0, 2, 1).reshape(nblk * BLOCK, -1)[:T]
         assert np.array_equal(k, lg["kb"]) and np.array_equal(v, lg["vb"])
         assert np.array_equal(lk, lg["lk"]) and np.array_equal(lv, lg["lv"])

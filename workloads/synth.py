@@ -21,7 +21,7 @@ bf16 once, and the oracle reads exactly the rounded value.
 Layouts handed to the library (block size 16):
 - ``k_base``  [NB, Hkv, 16, d]   token rows of one (block, head) contiguous
 - ``v_base``  [NB, Hkv, d, 16]   the 16 tokens of one (block, head, dim) contiguous
-- ``L_k`` pool [NB, 16, r]       token-major
+- ``L_k`` pool [NB, r/8, 16, 8]  chunks of 8 ranks (rank j of slot t at ((j/8)*16 + t)*8 + j%8)
 - ``L_v`` pool [NB, r, 16]       rank-major (16 tokens of one rank contiguous)
 - ``B_k``, ``B_v`` per agent [r, Hkv*d], column h*d + i
 """
@@ -245,7 +245,8 @@ class Workload:
         fill = (0x7FC0 if st == np.uint16 else np.nan) if poison else 0
         kpool = np.full((nb, H, BLOCK, d), fill, dtype=st)
         vpool = np.full((nb, H, d, BLOCK), fill, dtype=st)
-        lkp = [np.full((nb, BLOCK, r), fill, dtype=st) for r in self.pool_rank]
+        assert all(r % 8 == 0 for r in self.pool_rank), "low-rank pools hold chunks of 8 ranks"
+        lkp = [np.full((nb, r // 8, BLOCK, 8), fill, dtype=st) for r in self.pool_rank]
         lvp = [np.full((nb, r, BLOCK), fill, dtype=st) for r in self.pool_rank]
         bits = st == np.uint16
 
@@ -271,13 +272,14 @@ class Workload:
                 kpool[ids[nfull], :, :rem, :] = kbb[nfull, :, :rem, :]
                 vpool[ids[nfull], :, :, :rem] = vbb[nfull, :, :, :rem]
             for p in seg.pools:
-                lkb = blocks_of(lk[p])  # [nblk, 16, r]
+                lkb = blocks_of(lk[p])  # [nblk, 16, r] -> [nblk, r/8, 16, 8]
+                lkb = lkb.reshape(lkb.shape[0], BLOCK, -1, 8).transpose(0, 2, 1, 3)
                 lvb = blocks_of(lv[p]).transpose(0, 2, 1)  # [nblk, r, 16]
                 if nfull:
                     lkp[p][ids[:nfull]] = lkb[:nfull]
                     lvp[p][ids[:nfull]] = lvb[:nfull]
                 if rem:
-                    lkp[p][ids[nfull], :rem, :] = lkb[nfull, :rem, :]
+                    lkp[p][ids[nfull], :, :rem, :] = lkb[nfull, :, :rem, :]
                     lvp[p][ids[nfull], :, :rem] = lvb[nfull, :, :rem]
 
         # segments own disjoint blocks, so they fill in parallel
