@@ -87,10 +87,11 @@ struct Blk {
   static constexpr int KC = RP >= 32 ? RP / 32 : 1;
   static constexpr int NRT = RP / 16;
   bf16x8 kr[4];     // K_base[token lc][dims 32ks + 8lg .. +7]
-  uint2 vr[8];      // V^T[dim 16cb + lc][tokens 4lg .. +3]
+  uint2 vr[8];      // V^T[dim 16cb + lc][tokens 4lg .. +3] (RP 16); else as loaded, 16 bytes
+                    // per lane per pair of dim tiles (token_rows_to_operands)
   uint2 lk16;       // L_k[token lc][ranks 4lg .. +3]              (RP 16)
   bf16x8 lk32[KC];  // L_k[token lc][ranks 32kc + 8lg .. +7]       (RP 32, 64)
-  uint2 lv[NRT];    // L_v[rank 16rr + lc][tokens 4lg .. +3]
+  uint2 lv[NRT];    // L_v rows: RP 16: [rank lc][tokens 4lg .. +3]; else as loaded, like vr
 };
 
 // Low-rank rows of agents 1 .. NA-1 of the tile for one block (agent 0's
@@ -103,7 +104,7 @@ struct AgentRows {
   static constexpr int N = NA > 1 ? NA - 1 : 1;
   uint2 lk16[N];
   bf16x8 lk32[N][KC];
-  uint2 lv[N][NRT];
+  uint2 lv[N][NRT];  // as in Blk
 };
 
 struct WorkItem {

@@ -122,6 +122,26 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Rows of 16 tokens (a V^T dim row, an L_v rank row) read 16 bytes per lane:
+// lane (c, g) of the wave holds tokens 8(g&1) .. +7 of row 16(2t + (g>>1)) + c
+// for a pair of 16-row tiles t (a = its tokens +0..3, b = +4..7). Two row
+// swaps of 16 lanes and two of 32 lanes turn that into the 16x16x16 operands
+// of the two tiles (lane (c, g): tokens 4g .. 4g+3 of row c): a for tile 2t,
+// b for tile 2t + 1. One 16-byte load moves twice the bytes of an 8-byte one
+// at the same issue cost.
+__device__ __forceinline__ void token_rows_to_operands(uint2& a, uint2& b) {
+  const auto x = __builtin_amdgcn_permlane16_swap(a.x, b.x, false, false);
+  const auto y = __builtin_amdgcn_permlane16_swap(a.y, b.y, false, false);
+  const auto x2 = __builtin_amdgcn_permlane32_swap(x[0], x[1], false, false);
+  const auto y2 = __builtin_amdgcn_permlane32_swap(y[0], y[1], false, false);
+  a = make_uint2(x2[0], y2[0]);
+  b = make_uint2(x2[1], y2[1]);
+}
+// Byte offset of lane (c, g)'s 16-byte piece of tile pair t, rows of 16 tokens.
+__device__ __forceinline__ int token_rows_off(int t, int c, int g) {
+  return ((16 * (2 * t + (g >> 1)) + c) * 16 + 8 * (g & 1)) * 2;
+}
+
 // Offset of element (row, col) of a bf16 matrix of `nrows` rows and W
 // columns staged in LDS for MFMA operand reads, in which lane l reads row
 // l % 16 (plus a multiple of 16) at column group l / 16. Rows are not padded;
