@@ -94,15 +94,14 @@ __device__ __forceinline__ int opaque_if(int v) {
 
 // One producer wave's share of a 16-key cache block of a tile, on its way
 // from HBM: the whole block (NH = 1) or half of it (NH = 2: rotary pairs
-// 32 hh .. 32 hh + 31, and the V^T rows of parity hh in rank space or value
-// dims 64 hh .. 64 hh + 63 in the value rebuild).
+// 32 hh .. 32 hh + 31, and V^T rows (value dims) 64 hh .. 64 hh + 63).
 template <int RP, int NH, bool VREB>
 struct TileRegs {
   static constexpr int NCB = 4 / NH;  // 16-pair groups cb
   static constexpr int NPAR = 2 / NH; // V^T row parities (rank space)
   static constexpr int NDT = 8 / NH;  // 16-dim value tiles (value rebuild)
-  uint2 kbl[NCB], kbh[NCB];     // base keys of key lc: dims 16cb + 4lg .. +3 and +64
-  uint4 vv[VREB ? 1 : NPAR][2]; // rank space: V^T row 2 lane + parity, keys 8k .. +7 of the block (k = 0, 1)
+  uint2 kbl[NCB], kbh[NCB];     // base keys of key lc as loaded: 16 bytes per lane per pair of 16-dim tiles, and +64
+  uint4 vv[VREB ? 1 : NPAR][2]; // rank space: V^T row 64 u + 32k + lane/2, keys 8(lane&1) .. +7 of the block
   uint2 vb[VREB ? NDT : 1];     // value rebuild: base values of dim 16dt + lc, keys 4lg .. +3 of the block
   uint4 lk[RP == 64 ? 2 : 1];   // L_k row of key lc: ranks 8lg.. (RP 32/64) or 4lg.. (RP 16, .x .y)
   uint4 lvv[VREB ? (RP == 64 ? 2 : 1) : NPAR];  // L_v^T item lane + 64 u: rank item/2, keys 8 (item%2) .. +7
