@@ -71,7 +71,7 @@
 extern "C" {
 #endif
 
-#define LRA_VERSION 400
+#define LRA_VERSION 500
 
 typedef enum lra_status {
   LRA_OK = 0,
