@@ -94,14 +94,15 @@ struct Blk {
   uint2 lv[NRT];    // L_v rows: RP 16: [rank lc][tokens 4lg .. +3]; else as loaded, like vr
 };
 
-// Low-rank rows of agents 1 .. NA-1 of the tile for one block (agent 0's
-// travel with the block). Loaded only when the agents keep separate pools;
-// otherwise the loads get zero-length ranges.
-template <int RP, int NA>
+// Low-rank rows of the tile's agents for one block: of agents 1 .. NA-1
+// (ALL false: agent 0's travel with the block; loaded only when the agents
+// keep separate pools), or of every agent slot (ALL true; with shared pools
+// slot 0 holds the lead's rows and the others read nothing).
+template <int RP, int NA, bool ALL>
 struct AgentRows {
   static constexpr int KC = RP >= 32 ? RP / 32 : 1;
   static constexpr int NRT = RP / 16;
-  static constexpr int N = NA > 1 ? NA - 1 : 1;
+  static constexpr int N = ALL ? NA : (NA > 1 ? NA - 1 : 1);
   uint2 lk16[N];
   bf16x8 lk32[N][KC];
   uint2 lv[N][NRT];  // as in Blk
