@@ -23,8 +23,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const De
   using C = Cfg<RP, NA, KAD, VAD>;
   constexpr int HW = C::HW;
   constexpr int kRegion = C::kRegion;
-  __shared__ __align__(16) unsigned char s_region[kRegion];  // B_k^T [al][dim][k] in the loop, merge buffer after
-  __shared__ __align__(16) uint16_t s_bvt[VAD ? NA * D * RP : 8];          // B_v^T [al][dim][k]
+  // B_k^T [al][dim][k] in the loop (the merge buffer after it), then B_v^T
+  // [al][dim][k], in one array: the largest, so it is placed first and the
+  // adapter loop's B_k^T reads fit the 16-bit immediate offset of an LDS read
+  constexpr int kBvtBytes = (VAD ? NA * D * RP : 8) * 2;
+  __shared__ __align__(16) unsigned char s_lds0[kRegion + kBvtBytes];
+  unsigned char* const s_region = s_lds0;
+  uint16_t* const s_bvt = reinterpret_cast<uint16_t*>(s_lds0 + kRegion);
   __shared__ __align__(16) uint16_t s_q[16 * kQPitch];                     // query tile [row][dim]
   __shared__ __align__(16) uint16_t s_qp[KAD ? 16 * kQpPitch : 8];         // f16 query tile, k slots of the adapter product
   __shared__ __align__(16) f16x2 s_roff[KAD ? 16 * kRotPitch : 4];         // (cos, sin) of lc theta_i, [lc][i]
