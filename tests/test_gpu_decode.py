@@ -47,6 +47,8 @@ SMALL = [
     (32, 8, (6,), (513,), (64,) * 6, False, 5e5),  # 2 row tiles at r=64
     (32, 8, (1,) * 5, (31, 64, 257, 1500, 4097), (8, 16, 32, 64, 8), False, 5e5),  # mixed ranks
     (32, 4, (4,), (5000,), (16,) * 4, True, 5e5),
+    (32, 8, (4,), (700,), (64,) * 4, True, 5e5),  # one shared pool at r=64: its rows in slot 0, the rest empty
+    (32, 8, (4,), (301,), (32,) * 4, True, 0.0),  # the same at r=32, no rotary
 ]
 
 
