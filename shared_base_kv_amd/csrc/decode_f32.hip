@@ -10,13 +10,21 @@
 // share every chunk. Online softmax in the base-2 domain. A call without
 // key (value) adapters, or a sequence without an agent, takes rank 0 for
 // that part: its loops run zero times and its pools are not read.
+//
+// Every operand of a chunk is staged in LDS by coalesced 16-byte loads (base
+// keys, V^T, the low-rank rows of both pools), and the next chunk's loads are
+// in flight in registers while the current chunk is computed, so a chunk
+// costs one memory round trip at most; B_k is staged once per workgroup, B_v
+// once after the token loop (in the same LDS array).
 #include "device_common.h"
 #include "internal.h"
 
 namespace lra {
 namespace {
 
-constexpr int kChunk = 64;
+constexpr int kChunk = 64;  // tokens per chunk: 4 cache blocks
+constexpr int kF32Threads = 256;
+constexpr int kMaxRankF32 = 64;
 
 __device__ __forceinline__ float wave_max64(float v) {
 #pragma unroll
@@ -30,14 +38,20 @@ __device__ __forceinline__ float wave_sum64(float v) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArgs a) {
   constexpr int HALF = D / 2;
-  __shared__ float sK[kChunk][D + 1];
+  constexpr int kQK = kChunk * D / 4 / kF32Threads;            // 16-byte loads per thread: base keys (and values)
+  constexpr int kQL = kChunk * kMaxRankF32 / 4 / kF32Threads;  // ... low-rank rows of one pool (at most)
+  constexpr int kF4Blk = 4 * D;                                // 16-byte pieces of one block's keys (or values)
+  __shared__ float sK[kChunk][D + 1];           // keys of the chunk [token][dim]: base, then + rope(L_k B_k)
+  __shared__ float sV[D][kChunk + 1];           // V^T of the chunk [dim][token]
+  __shared__ float sLk[kChunk][kMaxRankF32 + 1];  // L_k rows [token][rank]
+  __shared__ float sLv[kMaxRankF32][kChunk + 1];  // L_v^T [rank][token]
+  __shared__ float sB[kMaxRankF32 * D];         // B_k [rank][dim] of head h; B_v after the token loop
   __shared__ float sQ[16][D];
   __shared__ float sP[16][kChunk];
   __shared__ float sM[16], sL[16], sAlpha[16];
-  __shared__ float sC[16][64];
-  __shared__ int sPhys[kChunk / kBlock];
+  __shared__ float sC[16][kMaxRankF32];
   __shared__ double sRev[kMaxRopePairs];
 
   const int s = blockIdx.x / a.Hkv;
@@ -61,39 +75,144 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
   const int* bt = a.block_tables + (size_t)s * a.max_blocks;
   const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
 
-  for (int e = tid; e < G * D; e += 256) {
+  for (int e = tid; e < G * D; e += kF32Threads) {
     const int row = e / D, i = e % D;
     sQ[row][i] = ((const float*)a.q)[((size_t)s * a.Hq + h * G + row) * D + i];
   }
+  for (int e = tid; e < rk * D; e += kF32Threads) sB[e] = bk[(size_t)(e / D) * HD + h * D + e % D];
   if (tid < kMaxRopePairs) sRev[tid] = a.rope_rev[tid];
   if (tid < 16) {
     sM[tid] = -INFINITY;
     sL[tid] = 0.f;
   }
-  constexpr int kAccPer = 16 * D / 256;  // (row, dim) pairs per thread
+
+  // ---- the chunk's loads into registers; pieces past the context (or before
+  // the activation point, for the low-rank rows) are zero ----
+  float4 rK[kQK], rV[kQK], rLk[kQL], rLv[kQL];
+  // Physical blocks of a chunk (-1 past the context): lane b of every wave
+  // loads entry b with a vector load (a scalar load would share its wait
+  // counter with the LDS reads of the compute), read out with readlane when
+  // the chunk's loads are issued. They are requested a chunk ahead.
+  int ids = -1, ph0, ph1, ph2, ph3;
+  auto fetch_ids = [&](int n0) __attribute__((always_inline)) {
+    ids = (lane < 4 && n0 + kBlock * lane < T) ? bt[n0 / kBlock + lane] : -1;
+  };
+  auto take_ids = [&]() __attribute__((always_inline)) {
+    ph0 = __builtin_amdgcn_readlane(ids, 0);
+    ph1 = __builtin_amdgcn_readlane(ids, 1);
+    ph2 = __builtin_amdgcn_readlane(ids, 2);
+    ph3 = __builtin_amdgcn_readlane(ids, 3);
+  };
+  auto block_of = [&](int b) __attribute__((always_inline)) {
+    return b == 0 ? ph0 : (b == 1 ? ph1 : (b == 2 ? ph2 : ph3));
+  };
+  auto fetch = [&](int n0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kQK; ++j) {
+      const int q = tid + kF32Threads * j, b = q / kF4Blk, f = 4 * (q % kF4Blk);
+      const int p = block_of(b);
+      const size_t base = ((size_t)(p < 0 ? 0 : p) * a.Hkv + h) * kBlock * D;
+      // keys: f = slot * D + i (one token per piece); values: f = i * 16 + slot (4 tokens)
+      rK[j] = (p >= 0 && n0 + kBlock * b + f / D < T) ? *reinterpret_cast<const float4*>(kb + base + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 v = p >= 0 ? *reinterpret_cast<const float4*>(vb + base + f) : make_float4(0.f, 0.f, 0.f, 0.f);
+      const int t0 = n0 + kBlock * b + f % kBlock;
+      v.x = t0 < T ? v.x : 0.f;
+      v.y = t0 + 1 < T ? v.y : 0.f;
+      v.z = t0 + 2 < T ? v.z : 0.f;
+      v.w = t0 + 3 < T ? v.w : 0.f;
+      rV[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < kQL; ++j) {
+      const int q = tid + kF32Threads * j;
+      float4 x = make_float4(0.f, 0.f, 0.f, 0.f), y = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (q < kBlock * rk) {  // L_k block: [r/8][16][8], f = (k/8) * 128 + slot * 8 + k % 8
+        const int b = q / (4 * rk), f = 4 * (q % (4 * rk));
+        const int p = block_of(b), n = n0 + kBlock * b + (f % 128) / 8;
+        if (p >= 0 && n < T && n >= act) x = *reinterpret_cast<const float4*>(lk + (size_t)p * kBlock * rk + f);
+      }
+      if (q < kBlock * rv) {  // L_v block: [r][16], f = k * 16 + slot
+        const int b = q / (4 * rv), f = 4 * (q % (4 * rv));
+        const int p = block_of(b), t0 = n0 + kBlock * b + f % kBlock;
+        if (p >= 0) y = *reinterpret_cast<const float4*>(lv + (size_t)p * kBlock * rv + f);
+        y.x = (t0 < T && t0 >= act) ? y.x : 0.f;
+        y.y = (t0 + 1 < T && t0 + 1 >= act) ? y.y : 0.f;
+        y.z = (t0 + 2 < T && t0 + 2 >= act) ? y.z : 0.f;
+        y.w = (t0 + 3 < T && t0 + 3 >= act) ? y.w : 0.f;
+      }
+      rLk[j] = x;
+      rLv[j] = y;
+    }
+  };
+  auto stage = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < kQK; ++j) {
+      const int q = tid + kF32Threads * j, b = q / kF4Blk, f = 4 * (q % kF4Blk);
+      const int t = kBlock * b + f / D, i = f % D;
+      sK[t][i] = rK[j].x;
+      sK[t][i + 1] = rK[j].y;
+      sK[t][i + 2] = rK[j].z;
+      sK[t][i + 3] = rK[j].w;
+      const int iv = f / kBlock, tv = kBlock * b + f % kBlock;
+      sV[iv][tv] = rV[j].x;
+      sV[iv][tv + 1] = rV[j].y;
+      sV[iv][tv + 2] = rV[j].z;
+      sV[iv][tv + 3] = rV[j].w;
+    }
+#pragma unroll
+    for (int j = 0; j < kQL; ++j) {
+      const int q = tid + kF32Threads * j;
+      if (q < kBlock * rk) {
+        const int b = q / (4 * rk), f = 4 * (q % (4 * rk));
+        const int t = kBlock * b + (f % 128) / 8, k = 8 * (f / 128) + f % 8;
+        sLk[t][k] = rLk[j].x;
+        sLk[t][k + 1] = rLk[j].y;
+        sLk[t][k + 2] = rLk[j].z;
+        sLk[t][k + 3] = rLk[j].w;
+      }
+      if (q < kBlock * rv) {
+        const int b = q / (4 * rv), f = 4 * (q % (4 * rv));
+        const int k = f / kBlock, t = kBlock * b + f % kBlock;
+        sLv[k][t] = rLv[j].x;
+        sLv[k][t + 1] = rLv[j].y;
+        sLv[k][t + 2] = rLv[j].z;
+        sLv[k][t + 3] = rLv[j].w;
+      }
+    }
+  };
+
+  constexpr int kAccPer = 16 * D / kF32Threads;  // (row, dim) pairs per thread
   float acc[kAccPer];
 #pragma unroll
   for (int i = 0; i < kAccPer; ++i) acc[i] = 0.f;
   float accC[4] = {0.f, 0.f, 0.f, 0.f};  // (row, k) pairs: 16 x 64 / 256
 
+  fetch_ids(0);
+  take_ids();
+  fetch(0);
+  fetch_ids(kChunk);
   for (int n0 = 0; n0 < T; n0 += kChunk) {
+    __syncthreads();  // the previous chunk's LDS reads are done
+    stage();
     __syncthreads();
-    if (tid < kChunk / kBlock) sPhys[tid] = (n0 + tid * kBlock < T) ? bt[n0 / kBlock + tid] : 0;
-    __syncthreads();
-    // rebuilt keys of this chunk: K = K_base + rope_n(L_k B_k)
-    for (int e = tid; e < kChunk * HALF; e += 256) {
-      const int t = e / HALF, i = e % HALF;
-      const int n = n0 + t;
-      float k1 = 0.f, k2 = 0.f;
-      if (n < T) {
-        const int phys = sPhys[t / kBlock], slot = n % kBlock;
+    if (n0 + kChunk < T) {  // in flight during this chunk's compute
+      take_ids();
+      fetch(n0 + kChunk);
+      fetch_ids(n0 + 2 * kChunk);
+    }
+    // rebuilt keys: K = K_base + rope_n(L_k B_k), pair (i, i + D/2) of token t
+    if (rk) {
+      for (int e = tid; e < kChunk * HALF; e += kF32Threads) {
+        const int t = e / HALF, i = e % HALF;
+        const int n = n0 + t;
+        if (n >= T || n < act) continue;
         float x1 = 0.f, x2 = 0.f;
-        for (int k = 0; k < (n >= act ? rk : 0); ++k) {
-          const float l = lk[(size_t)phys * kBlock * rk + ((k >> 3) * kBlock + slot) * 8 + (k & 7)];
-          x1 = fmaf(l, bk[(size_t)k * HD + h * D + i], x1);
-          x2 = fmaf(l, bk[(size_t)k * HD + h * D + i + HALF], x2);
+        for (int k = 0; k < rk; ++k) {
+          const float l = sLk[t][k];
+          x1 = fmaf(l, sB[k * D + i], x1);
+          x2 = fmaf(l, sB[k * D + i + HALF], x2);
         }
-        if (a.rope && rk) {
+        if (a.rope) {
           const double x = (double)n * sRev[i];
           const float f = (float)(x - __builtin_floor(x));
           const float c = __builtin_amdgcn_cosf(f), sn = __builtin_amdgcn_sinf(f);
@@ -101,19 +220,17 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
           x1 = y1;
           x2 = y2;
         }
-        const float* kp = kb + (size_t)phys * blk_elems + ((size_t)h * kBlock + slot) * D;
-        k1 = kp[i] + x1;
-        k2 = kp[i + HALF] + x2;
+        sK[t][i] += x1;
+        sK[t][i + HALF] += x2;
       }
-      sK[t][i] = k1;
-      sK[t][i + HALF] = k2;
+      __syncthreads();
     }
-    __syncthreads();
-    for (int e = tid; e < G * kChunk; e += 256) {
+    for (int e = tid; e < G * kChunk; e += kF32Threads) {
       const int row = e / kChunk, t = e % kChunk;
       float sc = -INFINITY;
       if (n0 + t < T) {
         float dot = 0.f;
+#pragma unroll 16
         for (int i = 0; i < D; ++i) dot = fmaf(sQ[row][i], sK[t][i], dot);
         sc = dot * a.sm_scale_log2;
       }
@@ -135,30 +252,27 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
       }
     }
     __syncthreads();
-    // O[row, i] += sum_t p V_base ;  C[row, k] += sum_t p L_v
+    // O[row, i] += sum_t p V_base ;  C[row, k] += sum_t p L_v (tokens past the
+    // context have p = 0 and zero rows)
 #pragma unroll
     for (int u = 0; u < kAccPer; ++u) {
-      const int e = tid + 256 * u;
+      const int e = tid + kF32Threads * u;
       const int row = e / D, i = e % D;
       if (row < G) {
         float v = acc[u] * sAlpha[row];
-        for (int t = 0; t < kChunk && n0 + t < T; ++t) {
-          const int phys = sPhys[t / kBlock];
-          v = fmaf(sP[row][t], vb[(size_t)phys * blk_elems + ((size_t)h * D + i) * kBlock + t % kBlock], v);
-        }
+#pragma unroll 16
+        for (int t = 0; t < kChunk; ++t) v = fmaf(sP[row][t], sV[i][t], v);
         acc[u] = v;
       }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int e = tid + 256 * u;
-      const int row = e / 64, k = e % 64;
+      const int e = tid + kF32Threads * u;
+      const int row = e / kMaxRankF32, k = e % kMaxRankF32;
       if (row < G && k < rv) {
         float v = accC[u] * sAlpha[row];
-        for (int t = (act > n0 ? act - n0 : 0); t < kChunk && n0 + t < T; ++t) {
-          const int phys = sPhys[t / kBlock];
-          v = fmaf(sP[row][t], lv[((size_t)phys * rv + k) * kBlock + t % kBlock], v);
-        }
+#pragma unroll 16
+        for (int t = 0; t < kChunk; ++t) v = fmaf(sP[row][t], sLv[k][t], v);
         accC[u] = v;
       }
     }
@@ -166,17 +280,18 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
-    const int e = tid + 256 * u;
-    sC[e / 64][e % 64] = accC[u];
+    const int e = tid + kF32Threads * u;
+    sC[e / kMaxRankF32][e % kMaxRankF32] = accC[u];
   }
+  for (int e = tid; e < rv * D; e += kF32Threads) sB[e] = bv[(size_t)(e / D) * HD + h * D + e % D];
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < kAccPer; ++u) {
-    const int e = tid + 256 * u;
+    const int e = tid + kF32Threads * u;
     const int row = e / D, i = e % D;
     if (row < G) {
       float v = acc[u];
-      for (int k = 0; k < rv; ++k) v = fmaf(sC[row][k], bv[(size_t)k * HD + h * D + i], v);
+      for (int k = 0; k < rv; ++k) v = fmaf(sC[row][k], sB[k * D + i], v);
       ((float*)a.out)[((size_t)s * a.Hq + h * G + row) * D + i] = v / sL[row];
     }
   }
@@ -185,7 +300,7 @@ __global__ __launch_bounds__(256) void decode_f32_kernel(const DecodeArgs a) {
 }  // namespace
 
 hipError_t launch_decode_f32(const DecodeArgs& a, hipStream_t stream) {
-  const dim3 grid(a.S * a.Hkv), block(256);
+  const dim3 grid(a.S * a.Hkv), block(kF32Threads);
   if (a.d == 64)
     hipLaunchKernelGGL(decode_f32_kernel<64>, grid, block, 0, stream, a);
   else if (a.d == 128)
