@@ -14,9 +14,13 @@ BUILD_DIR = os.path.join(os.path.dirname(HERE), "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -packed-fp32-ops: no v_pk_*_f32 anywhere (they are not used by this library).
+# kernarg preload: a kernel's leading scalar and pointer arguments, up to 14
+# dwords, arrive in SGPRs at wave start (the decode kernel's work-item fields);
+# a kernel whose first argument is a struct preloads nothing.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-x", "hip",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=14",
     "-Wall", "-Wno-unused-function",
 ]
 SOURCES = ["lra_api.cpp", "decode_bf16.hip", "decode_bf16_kv.hip", "decode_f32.hip", "lr_build.hip", "prefill_bf16.hip"]

@@ -18,8 +18,14 @@ using namespace dec;
 // is compiled in).
 // Writes the split's record (m, l, seq, nact, O' per row), or the finished
 // rows when the context fits one split.
+// The leading scalar arguments repeat fields of `a` that the preamble reads
+// first (DecodeHot), so they can be preloaded into SGPRs.
 template <int RP, int NA, bool KAD, bool VAD, bool ACT>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(const DecodeArgs a) {
+__global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(
+    const int32_t* context_lens, const int32_t* block_tables, const int32_t* agent_ids, const int32_t* group_offsets,
+    int n_work, int dims, int row_tiles, int split, int max_blocks, int S, const DecodeArgs a) {
+  const DecodeHot hp =
+      make_hot(context_lens, block_tables, agent_ids, group_offsets, n_work, dims, row_tiles, split, max_blocks, S);
   using C = Cfg<RP, NA, KAD, VAD>;
   constexpr int HW = C::HW;
   constexpr int kRegion = C::kRegion;
@@ -111,12 +117,19 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
   }
 }
 
+template <int RP, int NA, bool KAD, bool VAD, bool ACT>
+void launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
+  hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD, ACT>), grid, dim3(kDecodeWaves * 64), 0, stream,
+                     a.context_lens, a.block_tables, a.agent_ids, a.group_offsets, a.n_work,
+                     pack_hot_dims(a.nsplit, a.apt, a.Hkv), a.row_tiles, a.split, a.max_blocks, a.S, a);
+}
+
 template <int RP, int NA, bool KAD, bool VAD>
 void launch_main(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   if (a.act)
-    hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD, true>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+    launch_kernel<RP, NA, KAD, VAD, true>(a, grid, stream);
   else
-    hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD, false>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+    launch_kernel<RP, NA, KAD, VAD, false>(a, grid, stream);
 }
 
 template <bool KAD, bool VAD>
@@ -160,7 +173,7 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t s
   else if (kad)
     launched = launch_variant<true, false>(a, rp, na, grid, stream);
   else {  // no adapter: one variant serves every tile width (no per-agent state)
-    hipLaunchKernelGGL((decode_bf16_kernel<16, 1, false, false, false>), grid, dim3(kDecodeWaves * 64), 0, stream, a);
+    launch_kernel<16, 1, false, false, false>(a, grid, stream);
     launched = true;
   }
   if (!launched) return hipErrorInvalidValue;

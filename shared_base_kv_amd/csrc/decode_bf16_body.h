@@ -108,6 +108,42 @@ struct AgentRows {
   uint2 lv[N][NRT];  // as in Blk
 };
 
+// The argument fields the work-item preamble needs first. The kernel takes
+// them as leading scalar arguments (fourteen dwords, nsplit, apt and Hkv
+// packed in one), which the dispatch preloads into SGPRs when the library is
+// built with kernel-argument preloading: the first dependent loads (context
+// length, agent ids, block-table entries) then go out without waiting for a
+// read of the kernel-argument segment.
+struct DecodeHot {
+  const int32_t* context_lens;
+  const int32_t* block_tables;
+  const int32_t* agent_ids;
+  const int32_t* group_offsets;
+  int n_work, nsplit, apt, Hkv, row_tiles, split, max_blocks, S;
+};
+// nsplit (< 256), apt (< 256) and Hkv (< 65536) in one dword
+__host__ __device__ __forceinline__ int pack_hot_dims(int nsplit, int apt, int Hkv) {
+  return nsplit | (apt << 8) | (Hkv << 16);
+}
+__device__ __forceinline__ DecodeHot make_hot(const int32_t* context_lens, const int32_t* block_tables,
+                                              const int32_t* agent_ids, const int32_t* group_offsets, int n_work,
+                                              int dims, int row_tiles, int split, int max_blocks, int S) {
+  DecodeHot h;
+  h.context_lens = context_lens;
+  h.block_tables = block_tables;
+  h.agent_ids = agent_ids;
+  h.group_offsets = group_offsets;
+  h.n_work = n_work;
+  h.nsplit = dims & 0xff;
+  h.apt = (dims >> 8) & 0xff;
+  h.Hkv = (int)((unsigned)dims >> 16);
+  h.row_tiles = row_tiles;
+  h.split = split;
+  h.max_blocks = max_blocks;
+  h.S = S;
+  return h;
+}
+
 struct WorkItem {
   int g, rt, h, c, s_first, s0, ns, T, nact, t_begin, t_end, tile_id;
 };
@@ -119,7 +155,7 @@ struct WorkItem {
 // that L2 once).
 // First part: the group's sequences and the row tile's slots (false: the
 // tile has no sequences).
-__device__ __forceinline__ bool decode_item_rows(const DecodeArgs& a, int logical, WorkItem& w) {
+__device__ __forceinline__ bool decode_item_rows(const DecodeHot& a, int logical, WorkItem& w) {
   int rem = logical;
   w.h = rem % a.Hkv;
   rem /= a.Hkv;
@@ -135,7 +171,8 @@ __device__ __forceinline__ bool decode_item_rows(const DecodeArgs& a, int logica
     w.s_first = 0;
     s_end = a.S;
     if (w.g > 0) w.s_first = sload(a.group_offsets + w.g);
-    if (w.g + 1 < a.num_groups) s_end = sload(a.group_offsets + w.g + 1);
+    // not the last group: (g + 1) * items per group < n_work
+    if ((w.g + 1) * a.nsplit * a.row_tiles * a.Hkv < a.n_work) s_end = sload(a.group_offsets + w.g + 1);
   } else {
     w.s_first = w.g;
     s_end = w.g + 1;
@@ -145,9 +182,10 @@ __device__ __forceinline__ bool decode_item_rows(const DecodeArgs& a, int logica
   w.tile_id = (w.g * a.row_tiles + w.rt) * a.Hkv + w.h;
   return w.ns > 0;
 }
-// Second part: the group's context length and this split's token range.
-__device__ __forceinline__ void decode_item_span(const DecodeArgs& a, WorkItem& w) {
-  w.T = sload(a.context_lens + w.s_first);
+// Second part: this split's token range, from the group's context length T
+// (read by the caller from context_lens[s_first]).
+__device__ __forceinline__ void decode_item_span(const DecodeHot& a, WorkItem& w, int T) {
+  w.T = T;
   w.nact = (w.T + a.split - 1) / a.split;
   w.t_begin = w.c * a.split;
   w.t_end = min(w.T, w.t_begin + a.split);

@@ -81,6 +81,7 @@ int check_decode_sizes(int S, int num_groups, int Hq, int Hkv, int d, int max_ra
   if (Hq < 1 || Hkv < 1) return fail(LRA_ERR_INVALID_ARG, "Hq and Hkv must be >= 1 (got %d, %d)", Hq, Hkv);
   if (Hq % Hkv) return fail(LRA_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
   if (Hq / Hkv > 16) return fail(LRA_ERR_UNSUPPORTED, "at most 16 query heads per KV head (got %d)", Hq / Hkv);
+  if (Hkv > 65535) return fail(LRA_ERR_UNSUPPORTED, "at most 65535 KV heads (got %d)", Hkv);
   if (dtype != LRA_F32 && dtype != LRA_BF16) return fail(LRA_ERR_UNSUPPORTED, "dtype %d is not LRA_F32 or LRA_BF16", dtype);
   if (dtype == LRA_BF16 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "bf16 kernels are built for d = 128 (got %d)", d);
   if (dtype == LRA_F32 && d != 64 && d != 128) return fail(LRA_ERR_UNSUPPORTED, "fp32 kernel supports d = 64 or 128 (got %d)", d);
