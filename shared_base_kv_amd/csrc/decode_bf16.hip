@@ -117,6 +117,9 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
   }
 }
 
+static_assert(kNumXcd == 8, "the work-item dealing assumes 8 XCDs");
+int round_up8(int x) { return (x + 7) & ~7; }
+
 template <int RP, int NA, bool KAD, bool VAD, bool ACT>
 void launch_kernel(const DecodeArgs& a, dim3 grid, hipStream_t stream) {
   hipLaunchKernelGGL((decode_bf16_kernel<RP, NA, KAD, VAD, ACT>), grid, dim3(kDecodeWaves * 64), 0, stream,
@@ -161,8 +164,13 @@ bool launch_decode_bf16_kv(const DecodeArgs& a, int rp, int na, dim3 grid, hipSt
 }
 #else
 hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t stream) {
-  const int per = (a.n_work + kNumXcd - 1) / kNumXcd;
-  const dim3 grid(per * kNumXcd);
+  // grid: with several groups and 8 or more splits, groups and splits padded
+  // to multiples of 8 (dealt over the XCDs by the kernel); else
+  // n_work rounded up to 8
+  const int usz = a.row_tiles * a.Hkv;
+  const int n_grid = (a.nsplit >= kNumXcd && a.num_groups > 1) ? round_up8(a.num_groups) * round_up8(a.nsplit) * usz
+                                         : ((a.n_work + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  const dim3 grid(n_grid);
   const int n_rows = a.num_groups * a.row_tiles * a.Hkv * 16;
   const bool kad = a.bk != nullptr, vad = a.bv != nullptr;
   bool launched;
