@@ -202,15 +202,20 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
     }
     // rebuilt keys: K = K_base + rope_n(L_k B_k), pair (i, i + D/2) of token t
     if (rk) {
-      for (int e = tid; e < kChunk * HALF; e += kF32Threads) {
+#pragma unroll 4
+      for (int u = 0; u < kChunk * HALF / kF32Threads; ++u) {  // four pairs' reads in flight
+        const int e = tid + kF32Threads * u;
         const int t = e / HALF, i = e % HALF;
         const int n = n0 + t;
         if (n >= T || n < act) continue;
         float x1 = 0.f, x2 = 0.f;
-        for (int k = 0; k < rk; ++k) {
-          const float l = sLk[t][k];
-          x1 = fmaf(l, sB[k * D + i], x1);
-          x2 = fmaf(l, sB[k * D + i + HALF], x2);
+        for (int k0 = 0; k0 < rk; k0 += 8) {  // ranks are multiples of 8: eight reads in flight
+#pragma unroll
+          for (int k = k0; k < k0 + 8; ++k) {
+            const float l = sLk[t][k];
+            x1 = fmaf(l, sB[k * D + i], x1);
+            x2 = fmaf(l, sB[k * D + i + HALF], x2);
+          }
         }
         if (a.rope) {
           const double x = (double)n * sRev[i];
@@ -291,7 +296,9 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
     const int row = e / D, i = e % D;
     if (row < G) {
       float v = acc[u];
-      for (int k = 0; k < rv; ++k) v = fmaf(sC[row][k], sB[k * D + i], v);
+      for (int k0 = 0; k0 < rv; k0 += 8)
+#pragma unroll
+        for (int k = k0; k < k0 + 8; ++k) v = fmaf(sC[row][k], sB[k * D + i], v);
       ((float*)a.out)[((size_t)s * a.Hq + h * G + row) * D + i] = v / sL[row];
     }
   }
