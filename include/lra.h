@@ -162,7 +162,9 @@ int lr_cache_build_multi(const void* X, int64_t ldx, const void* A, int64_t lda,
  * keys 0..T_s-1 (T_s = context_lens[s] includes the current token).
  *
  *   q, out        [S, Hq, d]; q already rotated. out[s, j] for query head j
- *                 reads KV head j / (Hq/Hkv).
+ *                 reads KV head j / (Hq/Hkv). Hq a multiple of Hkv, at most 16
+ *                 query heads per KV head, Hkv <= 65535 (LRA_ERR_UNSUPPORTED
+ *                 beyond).
  *   block_tables  int32 [S, max_blocks]; entries past ceil(T_s/16) are not read.
  *   context_lens  int32 [S], 1 <= T_s <= max_blocks*16 and <= max_context_len.
  *   group_offsets int32 [num_groups+1] or NULL (every sequence its own group).
