@@ -49,6 +49,7 @@ def _decode(**over):
     (dict(q=FAKE + 2), B.LRA_ERR_INVALID_ARG, "aligned"),
     (dict(Hq=30), B.LRA_ERR_INVALID_ARG, "multiple"),
     (dict(Hq=8 * 17), B.LRA_ERR_UNSUPPORTED, "16 query heads"),
+    (dict(Hq=65536, Hkv=65536), B.LRA_ERR_UNSUPPORTED, "65535 KV heads"),
     (dict(d=64), B.LRA_ERR_UNSUPPORTED, "d = 128"),
     (dict(dtype=7), B.LRA_ERR_UNSUPPORTED, "dtype"),
     (dict(max_rank=65), B.LRA_ERR_UNSUPPORTED, "max_rank"),
