@@ -49,6 +49,10 @@ SMALL = [
     (32, 4, (4,), (5000,), (16,) * 4, True, 5e5),
     (32, 8, (4,), (700,), (64,) * 4, True, 5e5),  # one shared pool at r=64: its rows in slot 0, the rest empty
     (32, 8, (4,), (301,), (32,) * 4, True, 0.0),  # the same at r=32, no rotary
+    # several groups with 8 or more splits: splits dealt over the XCDs by
+    # (group + split), group and split counts padded to multiples of 8
+    (16, 4, (1, 2, 1), (6000, 2500, 4200), (16, 32, 16, 8), False, 5e5),  # 3 groups, 12 splits of 512
+    (4, 4, (10, 1), (5000, 3000), (16,) * 11, False, 5e5),  # 2 groups, 2 row tiles, 10 splits of 512
 ]
 
 
