@@ -26,15 +26,27 @@ constexpr int kChunk = 64;  // tokens per chunk: 4 cache blocks
 constexpr int kF32Threads = 256;
 constexpr int kMaxRankF32 = 64;
 
+// Reductions over the 64 lanes of a wave without an LDS round trip: DPP moves
+// within rows of 16 lanes (lanes 1 and 2 apart, then mirrored within 8 and
+// within 16), then the gfx950 row swaps across rows; every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
 __device__ __forceinline__ float wave_max64(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  return wave_max_across_groups(v);
 }
 __device__ __forceinline__ float wave_sum64(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
+  return wave_sum_across_groups(v);
 }
 
 template <int D>
@@ -234,10 +246,12 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
       const int row = e / kChunk, t = e % kChunk;
       float sc = -INFINITY;
       if (n0 + t < T) {
-        float dot = 0.f;
-#pragma unroll 16
-        for (int i = 0; i < D; ++i) dot = fmaf(sQ[row][i], sK[t][i], dot);
-        sc = dot * a.sm_scale_log2;
+        float d4[4] = {0.f, 0.f, 0.f, 0.f};  // four independent sums (short dependency chains)
+#pragma unroll
+        for (int i = 0; i < D; i += 4)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) d4[j] = fmaf(sQ[row][i + j], sK[t][i + j], d4[j]);
+        sc = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * a.sm_scale_log2;
       }
       sP[row][t] = sc;
     }
@@ -264,10 +278,12 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
       const int e = tid + kF32Threads * u;
       const int row = e / D, i = e % D;
       if (row < G) {
-        float v = acc[u] * sAlpha[row];
-#pragma unroll 16
-        for (int t = 0; t < kChunk; ++t) v = fmaf(sP[row][t], sV[i][t], v);
-        acc[u] = v;
+        float v4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kChunk; t += 4)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = fmaf(sP[row][t + j], sV[i][t + j], v4[j]);
+        acc[u] = acc[u] * sAlpha[row] + ((v4[0] + v4[1]) + (v4[2] + v4[3]));
       }
     }
 #pragma unroll
@@ -275,10 +291,12 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
       const int e = tid + kF32Threads * u;
       const int row = e / kMaxRankF32, k = e % kMaxRankF32;
       if (row < G && k < rv) {
-        float v = accC[u] * sAlpha[row];
-#pragma unroll 16
-        for (int t = 0; t < kChunk; ++t) v = fmaf(sP[row][t], sLv[k][t], v);
-        accC[u] = v;
+        float v4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < kChunk; t += 4)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v4[j] = fmaf(sP[row][t + j], sLv[k][t + j], v4[j]);
+        accC[u] = accC[u] * sAlpha[row] + ((v4[0] + v4[1]) + (v4[2] + v4[3]));
       }
     }
   }
