@@ -65,6 +65,7 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
   __shared__ float sM[16], sL[16], sAlpha[16];
   __shared__ float sC[16][kMaxRankF32];
   __shared__ double sRev[kMaxRopePairs];
+  __shared__ float sU[16][kMaxRankF32];         // without rotary: B_k q per query row
 
   const int s = blockIdx.x / a.Hkv;
   const int h = blockIdx.x % a.Hkv;
@@ -199,10 +200,27 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
   for (int i = 0; i < kAccPer; ++i) acc[i] = 0.f;
   float accC[4] = {0.f, 0.f, 0.f, 0.f};  // (row, k) pairs: 16 x 64 / 256
 
+  // Without the rotary embedding the adapter score needs no rebuilt key:
+  // q . (L_k[n] B_k) = L_k[n] . (B_k q), so u = B_k q is formed once per query
+  // row and each token's adapter score is an r-long dot product with its
+  // low-rank row (zero for tokens before the activation point).
+  const bool fold = rk > 0 && !a.rope;
   fetch_ids(0);
   take_ids();
   fetch(0);
   fetch_ids(kChunk);
+  if (fold) {
+    __syncthreads();  // sQ and B_k are staged
+    for (int e = tid; e < G * rk; e += kF32Threads) {
+      const int row = e / rk, k = e % rk;
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < D; i += 4)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) d4[j] = fmaf(sQ[row][i + j], sB[k * D + i + j], d4[j]);
+      sU[row][k] = (d4[0] + d4[1]) + (d4[2] + d4[3]);
+    }
+  }
   for (int n0 = 0; n0 < T; n0 += kChunk) {
     __syncthreads();  // the previous chunk's LDS reads are done
     stage();
@@ -213,7 +231,7 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
       fetch_ids(n0 + 2 * kChunk);
     }
     // rebuilt keys: K = K_base + rope_n(L_k B_k), pair (i, i + D/2) of token t
-    if (rk) {
+    if (rk && !fold) {
 #pragma unroll 4
       for (int u = 0; u < kChunk * HALF / kF32Threads; ++u) {  // four pairs' reads in flight
         const int e = tid + kF32Threads * u;
@@ -251,7 +269,12 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
         for (int i = 0; i < D; i += 4)
 #pragma unroll
           for (int j = 0; j < 4; ++j) d4[j] = fmaf(sQ[row][i + j], sK[t][i + j], d4[j]);
-        sc = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * a.sm_scale_log2;
+        float dl = 0.f;
+        if (fold)
+          for (int k0 = 0; k0 < rk; k0 += 8)
+#pragma unroll
+            for (int k = k0; k < k0 + 8; ++k) dl = fmaf(sLk[t][k], sU[row][k], dl);
+        sc = (((d4[0] + d4[1]) + (d4[2] + d4[3])) + dl) * a.sm_scale_log2;
       }
       sP[row][t] = sc;
     }
