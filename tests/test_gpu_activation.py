@@ -61,8 +61,9 @@ def test_agentless_and_starts_together():
     _check_decode(w, TOL_BF16)
 
 
-def test_f32_decode():
-    w = decode_workload(name="act_f32", dtype="f32", Hq=8, Hkv=4, d=64, theta=5e5, group_sizes=(3,),
+@pytest.mark.parametrize("theta", (5e5, 0.0))  # 0: the adapter score as L_k . (B_k q), no rebuilt key
+def test_f32_decode(theta):
+    w = decode_workload(name="act_f32", dtype="f32", Hq=8, Hkv=4, d=64, theta=theta, group_sizes=(3,),
                         context_lens=(150,), ranks=(8,) * 3, shared_l=False, seed=5, adapter_starts=(0, 70, 64))
     _check_decode(w, TOL_F32)
 

@@ -56,9 +56,10 @@ def test_small_decode(case, mode):
     _check_decode(w, TOL_BF16)
 
 
+@pytest.mark.parametrize("theta", (5e5, 0.0))  # 0: the adapter score as L_k . (B_k q), no rebuilt key
 @pytest.mark.parametrize("mode", MODES)
-def test_f32_decode(mode):
-    w = decode_workload(name="absent_f32", dtype="f32", Hq=8, Hkv=4, d=64, theta=5e5, group_sizes=(3,),
+def test_f32_decode(mode, theta):
+    w = decode_workload(name="absent_f32", dtype="f32", Hq=8, Hkv=4, d=64, theta=theta, group_sizes=(3,),
                         context_lens=(100,), ranks=(8,) * 3, shared_l=False, seed=3, adapt=mode)
     _check_decode(w, TOL_F32)
 
@@ -82,8 +83,9 @@ def test_agentless_sequences_in_decode(case, mode):
     _check_decode(w, TOL_BF16)
 
 
-def test_agentless_f32_decode():
-    w = decode_workload(name="agentless_f32", dtype="f32", Hq=8, Hkv=4, d=64, theta=5e5, group_sizes=(3,),
+@pytest.mark.parametrize("theta", (5e5, 0.0))
+def test_agentless_f32_decode(theta):
+    w = decode_workload(name="agentless_f32", dtype="f32", Hq=8, Hkv=4, d=64, theta=theta, group_sizes=(3,),
                         context_lens=(70,), agent_of_seq=(1, -1, 0), ranks=(8, 8), shared_l=False, seed=4)
     _check_decode(w, TOL_F32)
 
