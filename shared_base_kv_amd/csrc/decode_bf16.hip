@@ -84,12 +84,10 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
   const bool okc = lane < nact;
   const float m_c = __uint_as_float(hu.x), l_c = __uint_as_float(hu.y);
   float M = okc ? m_c : -INFINITY;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  M = wave_max64(M);
   const float w = okc ? fast_exp2(m_c - M) : 0.f;
   float L = okc ? w * l_c : 0.f;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+  L = wave_sum64(L);
   s_w[lane] = w;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_wave_barrier();

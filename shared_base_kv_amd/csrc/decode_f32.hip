@@ -26,29 +26,6 @@ constexpr int kChunk = 64;  // tokens per chunk: 4 cache blocks
 constexpr int kF32Threads = 256;
 constexpr int kMaxRankF32 = 64;
 
-// Reductions over the 64 lanes of a wave without an LDS round trip: DPP moves
-// within rows of 16 lanes (lanes 1 and 2 apart, then mirrored within 8 and
-// within 16), then the gfx950 row swaps across rows; every lane gets the result.
-template <int CTRL>
-__device__ __forceinline__ float dpp(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
-__device__ __forceinline__ float wave_max64(float v) {
-  v = fmaxf(v, dpp<kQuadXor1>(v));
-  v = fmaxf(v, dpp<kQuadXor2>(v));
-  v = fmaxf(v, dpp<kRowHalfMirror>(v));
-  v = fmaxf(v, dpp<kRowMirror>(v));
-  return wave_max_across_groups(v);
-}
-__device__ __forceinline__ float wave_sum64(float v) {
-  v += dpp<kQuadXor1>(v);
-  v += dpp<kQuadXor2>(v);
-  v += dpp<kRowHalfMirror>(v);
-  v += dpp<kRowMirror>(v);
-  return wave_sum_across_groups(v);
-}
-
 template <int D>
 __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArgs a) {
   constexpr int HALF = D / 2;

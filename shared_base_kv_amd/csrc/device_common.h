@@ -120,6 +120,29 @@ __device__ __forceinline__ float wave_sum_across_groups(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Reductions over the 64 lanes of a wave without an LDS round trip: DPP moves
+// within rows of 16 lanes (lanes 1 and 2 apart, then mirrored within 8 and
+// within 16), then the gfx950 row swaps across rows; every lane gets the result.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kQuadXor1 = 0xB1, kQuadXor2 = 0x4E, kRowHalfMirror = 0x141, kRowMirror = 0x140;
+__device__ __forceinline__ float wave_max64(float v) {
+  v = fmaxf(v, dpp<kQuadXor1>(v));
+  v = fmaxf(v, dpp<kQuadXor2>(v));
+  v = fmaxf(v, dpp<kRowHalfMirror>(v));
+  v = fmaxf(v, dpp<kRowMirror>(v));
+  return wave_max_across_groups(v);
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+  v += dpp<kQuadXor1>(v);
+  v += dpp<kQuadXor2>(v);
+  v += dpp<kRowHalfMirror>(v);
+  v += dpp<kRowMirror>(v);
+  return wave_sum_across_groups(v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Rows of 16 tokens (a V^T dim row, an L_v rank row) read 16 bytes per lane:
