@@ -631,7 +631,7 @@ def main():
                    "pool_copies_rotated": head["copies"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "decode_bf16_kernel<16, 4, true, true, false> + decode_bf16_combine", "algorithmic_bytes_per_launch": head["bytes"],
+                     "kernel": "decode_bf16_kernel<16, 4, true, true, false> + decode_bf16_combine<32>", "algorithmic_bytes_per_launch": head["bytes"],
                      "ms_per_launch": round(head["kernel_ms"], 5)},
         "per_launch_us": head["per_launch_us"],
     }

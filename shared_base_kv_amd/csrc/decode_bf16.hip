@@ -59,8 +59,12 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_bf16_kernel(
 // 1: finished by the main kernel). Lanes 0..31 take the even splits, lanes
 // 32..63 the odd ones, 4 output dims per lane; every load goes out at once
 // and loads past the records read zero through the buffer range check.
+// MS: a bound on the split count (32 or 64), so a call with at most 32
+// splits issues half the record loads.
+template <int MS>
 __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
-  __shared__ float s_w[kMaxSplits];
+  static_assert(MS == 32 || MS == 64, "split bound");
+  __shared__ float s_w[64];  // every lane writes its weight (zero past the splits)
   const int lane = threadIdx.x;
   const int gid = blockIdx.x;
   const int n_rows = a.num_groups * a.row_tiles * a.Hkv * 16;
@@ -72,9 +76,9 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
   const auto rs = buf_rsrc(pb, ((a.nsplit - 1) * cstride + a.part_stride) * 4);
   const uint4 hu = bld16(rs, lane < a.nsplit ? lane * cstride * 4 : kOob);
   const int half = lane >> 5, d4 = lane & 31;
-  uint4 v[kMaxSplits / 2];
+  uint4 v[MS / 2];
 #pragma unroll
-  for (int u = 0; u < kMaxSplits / 2; ++u) {
+  for (int u = 0; u < MS / 2; ++u) {
     const int c = 2 * u + half;
     v[u] = bld16(rs, c < a.nsplit ? (c * cstride + 4 + 4 * d4) * 4 : kOob);
   }
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(64) void decode_bf16_combine(const DecodeArgs a) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int u = 0; u < kMaxSplits / 2; ++u) {
+  for (int u = 0; u < MS / 2; ++u) {
     const int c = 2 * u + half;
     if (2 * u < nact) {  // uniform; records past nact are selected away, never multiplied
       const float wu = c < nact ? s_w[c] : 0.f;
@@ -185,7 +189,11 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, int rp, int na, hipStream_t s
   if (!launched) return hipErrorInvalidValue;
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.nsplit <= 1) return e;
-  hipLaunchKernelGGL(decode_bf16_combine, dim3(n_rows), dim3(64), 0, stream, a);
+  static_assert(kMaxSplits == 64, "combine variants cover up to 64 splits");
+  if (a.nsplit <= 32)
+    hipLaunchKernelGGL(decode_bf16_combine<32>, dim3(n_rows), dim3(64), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_bf16_combine<64>, dim3(n_rows), dim3(64), 0, stream, a);
   return hipGetLastError();
 }
 
