@@ -54,6 +54,7 @@ SMALL = [
     (16, 4, (1, 2, 1), (6000, 2500, 4200), (16, 32, 16, 8), False, 5e5),  # 3 groups, 12 splits of 512
     (4, 4, (10, 1), (5000, 3000), (16,) * 11, False, 5e5),  # 2 groups, 2 row tiles, 10 splits of 512
     (4, 1, (2,), (16000,), (16, 16), True, 5e5),  # one KV head: 63 splits of 256 (the 64-split combine)
+    (260, 260, (1,), (40,), (16,), True, 5e5),  # more than 255 KV heads (their count takes 16 bits of a packed argument)
 ]
 
 
