@@ -63,7 +63,6 @@ __global__ __launch_bounds__(kF32Threads) void decode_f32_kernel(const DecodeArg
   const float* vb = (const float*)a.vb;
   const int T = a.context_lens[s];
   const int* bt = a.block_tables + (size_t)s * a.max_blocks;
-  const size_t blk_elems = (size_t)a.Hkv * kBlock * D;
 
   for (int e = tid; e < G * D; e += kF32Threads) {
     const int row = e / D, i = e % D;
